@@ -1,0 +1,115 @@
+// Host side of libmoe: error state, device properties, capacity, the
+// whole-layer entry point and its workspace.
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "common.h"
+
+namespace moe {
+
+namespace {
+thread_local std::string g_last_error;
+}
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+void clear_error() { g_last_error.clear(); }
+
+const DeviceInfo& device_info() {
+  static std::mutex mu;
+  static std::vector<DeviceInfo> cache;
+  static std::vector<bool> have;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)cache.size() <= dev) {
+    cache.resize(dev + 1);
+    have.resize(dev + 1, false);
+  }
+  if (!have[dev]) {
+    DeviceInfo info{256, 160 * 1024};
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      info.cus = v;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess &&
+        v > 0)
+      info.lds_bytes = v;
+    cache[dev] = info;
+    have[dev] = true;
+  }
+  return cache[dev];
+}
+
+moe_status expert_ffn_impl(const moe_ffn_args* a, void* ws, size_t ws_bytes, hipStream_t stream,
+                           hipEvent_t mid_event);
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+// ceil(cf * T * k / E) exactly: cf = m * 2^ex with an integer mantissa m, so
+// the quotient is a ratio of integers evaluated in 128-bit arithmetic.
+extern "C" int32_t moe_capacity(int64_t T, int32_t k, int32_t E, double cf) {
+  if (!(cf > 0.0) || E <= 0 || T < 0 || k <= 0) return INT32_MAX;
+  int ex = 0;
+  const double fr = frexp(cf, &ex);                // cf = fr * 2^ex, fr in [0.5, 1)
+  const int64_t m = (int64_t)ldexp(fr, 53);        // exact 53-bit integer
+  ex -= 53;                                        // cf = m * 2^ex
+  unsigned __int128 num = (unsigned __int128)m * (unsigned __int128)T * (unsigned __int128)k;
+  unsigned __int128 den = (unsigned __int128)E;
+  if (ex >= 0) {
+    if (ex > 60) return INT32_MAX;
+    const unsigned __int128 big = num << ex;
+    if ((big >> ex) != num) return INT32_MAX;
+    num = big;
+  } else {
+    if (-ex > 100) {
+      // cf is tiny: ceil of a positive value below 1 (T*k > 0) is 1
+      return (T > 0) ? 1 : 0;
+    }
+    den <<= -ex;
+  }
+  unsigned __int128 q = num / den;
+  if (num % den) q += 1;
+  if (q > (unsigned __int128)INT32_MAX) return INT32_MAX;
+  return (int32_t)q;
+}
+
+extern "C" size_t moe_workspace_bytes(const moe_layer_args* a) {
+  if (!a) return 0;
+  size_t w = moe_route_workspace_bytes(&a->route);
+  const size_t d = moe_dispatch_workspace_bytes(&a->dispatch);
+  const size_t f = moe_ffn_workspace_bytes(&a->ffn);
+  if (d > w) w = d;
+  if (f > w) w = f;
+  return w;
+}
+
+extern "C" moe_status moe_layer_forward(const moe_layer_args* a, void* ws, size_t ws_bytes,
+                                        hipStream_t stream) {
+  clear_error();
+  MOE_CHECK_ARG(a != nullptr, "null args");
+  const size_t need = moe_workspace_bytes(a);
+  if (ws_bytes < need || (need && !ws)) {
+    set_error("moe_layer_forward: workspace too small");
+    return MOE_ERR_WORKSPACE;
+  }
+  hipEvent_t* ev = a->events;
+  if (ev) MOE_CHECK_HIP(hipEventRecord(ev[0], stream));
+  moe_status st = moe_route(&a->route, ws, ws_bytes, stream);
+  if (st != MOE_OK) return st;
+  if (ev) MOE_CHECK_HIP(hipEventRecord(ev[1], stream));
+  st = moe_dispatch(&a->dispatch, ws, ws_bytes, stream);
+  if (st != MOE_OK) return st;
+  if (ev) MOE_CHECK_HIP(hipEventRecord(ev[2], stream));
+  st = expert_ffn_impl(&a->ffn, ws, ws_bytes, stream, ev ? ev[3] : nullptr);
+  if (st != MOE_OK) return st;
+  if (ev) MOE_CHECK_HIP(hipEventRecord(ev[4], stream));
+  st = moe_combine(&a->combine, stream);
+  if (st != MOE_OK) return st;
+  if (ev) MOE_CHECK_HIP(hipEventRecord(ev[5], stream));
+  return MOE_OK;
+}

@@ -1,0 +1,273 @@
+// Dispatch: histogram, capacity drop, offsets, stable permutation and row
+// pack into the rank-major / expert-major send buffer (gfx950).
+//
+// What is computed follows the Ultralytics glossary "Expert Parallelism":
+// per-expert and per-rank assignment counts (the listing's bincount lines),
+// ranks owning contiguous expert blocks (rank = e // (E/R) in the listing),
+// and the capacity limit of "Load Balancing and Capacity" (an expert keeps at
+// most C assignments; overflow skips the expert).  Token order inside every
+// expert segment is preserved (mbrenndoerfer "Expert Parallelism > Summary",
+// buffer-management bullet), which also fixes which assignments are dropped:
+// the ones past the first C in token-major order.
+//
+// Three kernels, no ordering atomics (results are deterministic):
+//   hist_kernel      : block b owns a chunk of TB tokens (TB*k <= 256
+//                      assignments); LDS-private histogram -> blk[b][e].
+//   scan_kernel      : one workgroup; per expert an exclusive scan over blocks
+//                      (in place in blk), counts, kept = min(counts, C), the
+//                      expert offsets by a wave-level scan, per-rank counts.
+//   rank_pack_kernel : recomputes each assignment's position: block base +
+//                      earlier waves of the block + lanes of its wave holding
+//                      the same expert (ballot / popcount), which is exactly
+//                      the token-major position.  Writes slot and src, then
+//                      copies each token's row once from x into its kept slots
+//                      with 128-bit loads and stores (x is read once).
+#include "common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+__global__ void __launch_bounds__(kThreads) hist_kernel(const int32_t* __restrict__ ids,
+                                                       int32_t* __restrict__ blk, int64_t n_assign,
+                                                       int per_block, int E) {
+  __shared__ int cnt[MOE_MAX_EXPERTS];
+  for (int e = threadIdx.x; e < E; e += kThreads) cnt[e] = 0;
+  __syncthreads();
+  const int64_t g = (int64_t)blockIdx.x * per_block + threadIdx.x;
+  if (threadIdx.x < per_block && g < n_assign) {
+    const int e = ids[g];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);  // ids outside [0, E) are ignored
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kThreads) blk[(int64_t)blockIdx.x * E + e] = cnt[e];
+}
+
+// Inclusive scan of one value per thread across a 256-thread block.
+__device__ int block_inclusive_scan(int v, int* sh_waves) {
+  const int lane = lane_id();
+  const int w = threadIdx.x / 64;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(v, off, 64);
+    if (lane >= off) v += o;
+  }
+  if (lane == 63) sh_waves[w] = v;
+  __syncthreads();
+  int add = 0;
+  for (int i = 0; i < w; ++i) add += sh_waves[i];
+  __syncthreads();
+  return v + add;
+}
+
+__global__ void __launch_bounds__(kThreads) scan_kernel(
+    int32_t* __restrict__ blk, int nblocks, int E, int R, int C, int32_t* __restrict__ counts,
+    int32_t* __restrict__ kept, int32_t* __restrict__ off, int32_t* __restrict__ rank_counts,
+    int32_t* __restrict__ rank_off) {
+  __shared__ int sh_waves[kWaves];
+  __shared__ int sh_off[MOE_MAX_EXPERTS + 1];
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < E) {
+    int b = 0;
+    for (; b + 4 <= nblocks; b += 4) {
+      int v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = blk[(int64_t)(b + i) * E + e];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        blk[(int64_t)(b + i) * E + e] = total;
+        total += v[i];
+      }
+    }
+    for (; b < nblocks; ++b) {
+      const int v = blk[(int64_t)b * E + e];
+      blk[(int64_t)b * E + e] = total;
+      total += v;
+    }
+  }
+  const int kp = (e < E) ? min(total, C) : 0;
+  const int incl = block_inclusive_scan(kp, sh_waves);
+  if (e < E) {
+    counts[e] = total;
+    kept[e] = kp;
+    off[e] = incl - kp;
+    sh_off[e] = incl - kp;
+  }
+  if (e == E - 1) {
+    off[E] = incl;
+    sh_off[E] = incl;
+  }
+  __syncthreads();
+  const int per = E / R;
+  for (int r = threadIdx.x; r < R; r += kThreads) {
+    rank_counts[r] = sh_off[(r + 1) * per] - sh_off[r * per];
+    rank_off[r] = sh_off[r * per];
+  }
+  if (threadIdx.x == 0) rank_off[R] = sh_off[E];
+}
+
+template <int UNROLL>
+__global__ void __launch_bounds__(kThreads) rank_pack_kernel(
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ blk_base,
+    const int32_t* __restrict__ off, const u32x4* __restrict__ x, int32_t* __restrict__ slot_out,
+    int32_t* __restrict__ src_out, u32x4* __restrict__ x_send, int64_t T, int k, int E, int C,
+    int tokens_per_block, int row16) {
+  __shared__ int wcnt[kWaves][MOE_MAX_EXPERTS];
+  __shared__ int sl[kThreads];
+  const int lane = lane_id();
+  const int w = threadIdx.x / 64;
+  const int per_block = tokens_per_block * k;
+  const int64_t n_assign = T * k;
+  for (int i = threadIdx.x; i < kWaves * MOE_MAX_EXPERTS; i += kThreads) (&wcnt[0][0])[i] = 0;
+  __syncthreads();
+  const int64_t g = (int64_t)blockIdx.x * per_block + threadIdx.x;
+  const bool in_range = threadIdx.x < per_block && g < n_assign;
+  const int e = in_range ? ids[g] : -1;
+  const bool valid = in_range && e >= 0 && e < E;
+  if (valid) atomicAdd(&wcnt[w][e], 1);
+  __syncthreads();
+  // per-wave bases: block base + counts of the earlier waves
+  for (int ee = threadIdx.x; ee < E; ee += kThreads) {
+    int run = blk_base[(int64_t)blockIdx.x * E + ee];
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+      const int c = wcnt[i][ee];
+      wcnt[i][ee] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  // rank among the lanes of this wave with the same expert (token order)
+  uint64_t todo = ballot(valid);
+  int r = 0;
+  while (todo) {
+    const int leader = __ffsll((long long)todo) - 1;
+    const int el = __shfl(e, leader, 64);
+    const uint64_t m = ballot(valid && e == el);
+    if (valid && e == el) r = popc64(m & lanemask_lt());
+    todo &= ~m;
+  }
+  int s = -1;
+  if (valid) {
+    const int pos = wcnt[w][e] + r;
+    if (pos < C) {
+      s = off[e] + pos;
+      src_out[s] = (int32_t)(g / k);
+    }
+  }
+  if (in_range) slot_out[g] = s;
+  sl[threadIdx.x] = s;
+  __syncthreads();
+  // row pack: each token's row is read once and written to its kept slots
+  const int64_t t0 = (int64_t)blockIdx.x * tokens_per_block;
+  for (int tt = w; tt < tokens_per_block; tt += kWaves) {
+    const int64_t t = t0 + tt;
+    if (t >= T) break;
+    int sj[MOE_MAX_TOPK];
+    bool any = false;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      sj[j] = j < k ? sl[tt * k + j] : -1;
+      any |= sj[j] >= 0;
+    }
+    if (!any) continue;
+    const u32x4* xr = x + t * row16;
+    for (int c0 = lane; c0 < row16; c0 += 64 * UNROLL) {
+      u32x4 v[UNROLL];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const int c = c0 + u * 64;
+        if (c < row16) v[u] = xr[c];
+      }
+#pragma unroll
+      for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+        if (sj[j] < 0) continue;
+        u32x4* dst = x_send + (int64_t)sj[j] * row16;
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+          const int c = c0 + u * 64;
+          if (c < row16) dst[c] = v[u];
+        }
+      }
+    }
+  }
+}
+
+struct Plan {
+  int tokens_per_block;
+  int nblocks;
+};
+
+Plan plan_for(int64_t T, int k) {
+  int tb = kThreads / k;  // TB*k <= 256
+  const int64_t target_blocks = 2 * (int64_t)device_info().cus;
+  const int64_t small = (T + target_blocks - 1) / target_blocks;
+  if (small < tb) tb = (int)(small < 1 ? 1 : small);
+  Plan p;
+  p.tokens_per_block = tb;
+  p.nblocks = (int)((T + tb - 1) / tb);
+  return p;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int64_t moe_send_rows_max(int64_t T, int32_t k, int32_t E, int32_t capacity) {
+  const int64_t a = T * (int64_t)k;
+  const int64_t b = (int64_t)E * (int64_t)capacity;
+  return a < b ? a : b;
+}
+
+extern "C" size_t moe_dispatch_workspace_bytes(const moe_dispatch_args* a) {
+  if (!a || a->T <= 0 || a->k <= 0) return 0;
+  const Plan p = plan_for(a->T, a->k);
+  return align_up((size_t)p.nblocks * a->E * sizeof(int32_t), 256);
+}
+
+extern "C" moe_status moe_dispatch(const moe_dispatch_args* a, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+  clear_error();
+  MOE_CHECK_ARG(a != nullptr, "null args");
+  MOE_CHECK_ARG(a->T >= 0, "T < 0");
+  MOE_CHECK_ARG(a->E >= 1 && a->E <= MOE_MAX_EXPERTS, "E out of range [1, 256]");
+  MOE_CHECK_ARG(a->k >= 1 && a->k <= MOE_MAX_TOPK && a->k <= a->E, "k out of range [1, min(8, E)]");
+  MOE_CHECK_ARG(a->R >= 1 && a->E % a->R == 0, "E must be a positive multiple of R");
+  MOE_CHECK_ARG(a->capacity >= 0, "capacity < 0");
+  MOE_CHECK_ARG(a->act_dtype == MOE_F32 || a->act_dtype == MOE_BF16, "bad act_dtype");
+  const int es = a->act_dtype == MOE_F32 ? 4 : 2;
+  MOE_CHECK_ARG(a->d >= 1 && ((int64_t)a->d * es) % 16 == 0, "row of x must be a multiple of 16 bytes");
+  MOE_CHECK_ARG(a->T * (int64_t)a->k < (int64_t)1 << 31, "T*k must fit in int32");
+  MOE_CHECK_ARG(a->counts && a->kept && a->expert_off && a->rank_counts && a->rank_off,
+                "count/offset outputs are required");
+  MOE_CHECK_ARG(a->ids && a->slot && a->src && a->x && a->x_send, "null data pointer");
+  MOE_CHECK_ARG(aligned16(a->x) && aligned16(a->x_send), "x/x_send not 16-byte aligned");
+  const int row16 = (int)((int64_t)a->d * es / 16);
+  const Plan p = plan_for(a->T, a->k);
+  const size_t need = moe_dispatch_workspace_bytes(a);
+  if (a->T > 0 && (ws_bytes < need || ws == nullptr)) {
+    set_error("moe_dispatch: workspace too small");
+    return MOE_ERR_WORKSPACE;
+  }
+  int32_t* blk = static_cast<int32_t*>(ws);
+  if (a->T > 0) {
+    hist_kernel<<<p.nblocks, kThreads, 0, stream>>>(a->ids, blk, a->T * a->k,
+                                                     p.tokens_per_block * a->k, a->E);
+    MOE_CHECK_LAUNCH();
+  }
+  scan_kernel<<<1, kThreads, 0, stream>>>(blk, a->T > 0 ? p.nblocks : 0, a->E, a->R, a->capacity,
+                                          a->counts, a->kept, a->expert_off, a->rank_counts,
+                                          a->rank_off);
+  MOE_CHECK_LAUNCH();
+  if (a->T > 0) {
+    rank_pack_kernel<4><<<p.nblocks, kThreads, 0, stream>>>(
+        a->ids, blk, a->expert_off, (const u32x4*)a->x, a->slot, a->src, (u32x4*)a->x_send, a->T,
+        a->k, a->E, a->capacity, p.tokens_per_block, row16);
+    MOE_CHECK_LAUNCH();
+  }
+  return MOE_OK;
+}

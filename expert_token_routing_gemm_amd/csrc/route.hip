@@ -1,0 +1,485 @@
+// Route: router logits, scores and top-k (gfx950).
+//
+// Ultralytics glossary "Expert Parallelism", "How Tokens Move Between GPUs",
+// step 1: the router is a linear layer that scores every token against every
+// expert and keeps the top k.  The score function, weight renormalisation and
+// tie order are not on the pages: softmax or sigmoid, optional
+// renormalisation over the selected experts, ties to the lower expert index.
+// The selection-only bias follows "Load Balancing and Capacity" (bias-based
+// balancing bullet): it enters the selection key and nothing else.
+//
+// Kernels
+//   route_small_kernel : E <= 8 and W_r fits in LDS.  One pass over x with
+//                        W_r staged in LDS, fp32 VALU dot products, wave
+//                        butterfly reduction, top-k and weights fused.  The
+//                        op is HBM-bound (2E/s_a <= 8 flop per byte of x).
+//   logits_valu_kernel : any E, W_r read through L2; writes fp32 logits.
+//   topk_kernel        : one wave per token over fp32 logits in memory,
+//                        E <= 256; wavefront-shuffle arg-max k times.
+// Large E (E % 64 == 0, bf16) computes the logits with the bf16 MFMA GEMM of
+// the expert FFN (router intensity 2E/s_a is 64-256 flop/B there, above the
+// VALU ridge), then runs topk_kernel.
+#include "common.h"
+#include "gemm.h"
+
+namespace moe {
+namespace {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- helpers
+
+__device__ __forceinline__ bool key_better(float ka, int ia, float kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+
+// fp32 of sigmoid evaluated in double: the selection key precision.
+__device__ __forceinline__ float sigmoid_f32_via_f64(float x) {
+  return (float)(1.0 / (1.0 + exp(-(double)x)));
+}
+
+template <typename T>
+struct Vec16;  // 16 bytes of T, widened to floats
+
+template <>
+struct Vec16<float> {
+  static constexpr int N = 4;
+  __device__ __forceinline__ static void load(const void* p, float* out) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+  }
+};
+
+template <>
+struct Vec16<bf16_t> {
+  static constexpr int N = 8;
+  __device__ __forceinline__ static void load(const void* p, float* out) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+
+// Scores, top-k and weights of one token from its E (<= 8) final logits.
+template <int EMAX>
+__device__ void finish_token_small(const float* L, int E, int k, int score, int renorm,
+                                   const float* __restrict__ b_select, int64_t t,
+                                   int32_t* __restrict__ ids, float* __restrict__ weights) {
+  float key[EMAX];
+  float sc[EMAX];
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) {
+    if (e < E) {
+      if (score == MOE_SIGMOID) {
+        sc[e] = sigmoid_f32_via_f64(L[e]);
+        key[e] = b_select ? sc[e] + b_select[e] : sc[e];
+      } else {
+        key[e] = L[e];
+      }
+    } else {
+      key[e] = -INFINITY;
+    }
+  }
+  bool taken[EMAX];
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) taken[e] = false;
+  int sel[MOE_MAX_TOPK];
+  for (int j = 0; j < k; ++j) {
+    int best = -1;
+    float bk = 0.f;
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) {
+      if (e < E && !taken[e] && (best < 0 || key_better(key[e], e, bk, best))) {
+        best = e;
+        bk = key[e];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) taken[e] = taken[e] || (e == best);
+    sel[j] = best;
+  }
+  // weights
+  float wsel[MOE_MAX_TOPK];
+  float denom = 0.f;
+  if (score == MOE_SOFTMAX) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e)
+      if (e < E) m = fmaxf(m, L[e]);
+    float all = 0.f;
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e)
+      if (e < E) all += __expf(L[e] - m);
+    for (int j = 0; j < k; ++j) {
+      float v = 0.f;
+#pragma unroll
+      for (int e = 0; e < EMAX; ++e)
+        if (e == sel[j]) v = L[e];
+      wsel[j] = __expf(v - m);
+      denom += wsel[j];
+    }
+    if (!renorm) denom = all;
+  } else {
+    for (int j = 0; j < k; ++j) {
+      float v = 0.f;
+#pragma unroll
+      for (int e = 0; e < EMAX; ++e)
+        if (e == sel[j]) v = sc[e];
+      wsel[j] = v;
+      denom += v;
+    }
+    if (!renorm) denom = 1.f;
+  }
+  const float inv = 1.f / denom;
+  for (int j = 0; j < k; ++j) {
+    ids[t * k + j] = sel[j];
+    weights[t * k + j] = wsel[j] * inv;
+  }
+}
+
+// ---------------------------------------------------------------- E <= 8 fused
+// Block = 4 waves; each wave owns TPW tokens at a time.  Lane l covers the
+// 16-byte chunks l, l+64, ... of a row (coalesced 128-bit loads of x).
+template <typename T, int TPW>
+__global__ void __launch_bounds__(256) route_small_kernel(
+    const T* __restrict__ x, const T* __restrict__ wr, const float* __restrict__ b_router,
+    const float* __restrict__ b_select, float* __restrict__ logits_out, int32_t* __restrict__ ids,
+    float* __restrict__ weights, int64_t T_tok, int d, int E, int k, int score, int renorm) {
+  constexpr int EMAX = 8;
+  constexpr int VN = Vec16<T>::N;  // elements per 16 B
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  T* sw = reinterpret_cast<T*>(smem_raw);  // [E][d]
+  {
+    const int n16 = E * d / VN;
+    const uint4* g = reinterpret_cast<const uint4*>(wr);
+    uint4* s = reinterpret_cast<uint4*>(sw);
+    for (int i = threadIdx.x; i < n16; i += blockDim.x) s[i] = g[i];
+  }
+  __syncthreads();
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int nchunk = d / VN;  // 16-byte chunks per row
+  const int64_t waves_total = (int64_t)gridDim.x * (blockDim.x / kWave);
+  for (int64_t t0 = ((int64_t)blockIdx.x * (blockDim.x / kWave) + wave) * TPW; t0 < T_tok;
+       t0 += waves_total * TPW) {
+    float acc[TPW][EMAX];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+#pragma unroll
+      for (int e = 0; e < EMAX; ++e) acc[i][e] = 0.f;
+    for (int c = lane; c < nchunk; c += kWave) {
+      float xv[TPW][VN];
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        const int64_t t = t0 + i;
+        if (t < T_tok) {
+          Vec16<T>::load(x + t * d + (int64_t)c * VN, xv[i]);
+        } else {
+#pragma unroll
+          for (int v = 0; v < VN; ++v) xv[i][v] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < EMAX; ++e) {
+        if (e < E) {
+          float wv[VN];
+          Vec16<T>::load(sw + (int64_t)e * d + c * VN, wv);
+#pragma unroll
+          for (int i = 0; i < TPW; ++i)
+#pragma unroll
+            for (int v = 0; v < VN; ++v) acc[i][e] = fmaf(xv[i][v], wv[v], acc[i][e]);
+        }
+      }
+    }
+    // butterfly: every lane ends with the full sums
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+      for (int i = 0; i < TPW; ++i)
+#pragma unroll
+        for (int e = 0; e < EMAX; ++e) acc[i][e] += __shfl_xor(acc[i][e], off, kWave);
+    if (lane < TPW) {
+      const int64_t t = t0 + lane;
+      if (t < T_tok) {
+        float L[EMAX];
+#pragma unroll
+        for (int e = 0; e < EMAX; ++e) {
+          float v = 0.f;
+#pragma unroll
+          for (int i = 0; i < TPW; ++i)
+            if (i == lane) v = acc[i][e];
+          L[e] = (e < E) ? v + (b_router ? b_router[e] : 0.f) : 0.f;
+        }
+        if (logits_out) {
+          for (int e = 0; e < E; ++e) logits_out[t * E + e] = L[e];
+        }
+        finish_token_small<EMAX>(L, E, k, score, renorm, b_select, t, ids, weights);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- generic logits
+// logits[t, e] = x[t] . wr[e] for e in an 8-expert slice (blockIdx.y), no bias.
+template <typename T, int TPW>
+__global__ void __launch_bounds__(256) logits_valu_kernel(const T* __restrict__ x,
+                                                         const T* __restrict__ wr,
+                                                         float* __restrict__ logits,
+                                                         int64_t T_tok, int d, int E) {
+  constexpr int ES = 8;
+  constexpr int VN = Vec16<T>::N;
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int e0 = blockIdx.y * ES;
+  const int nchunk = d / VN;
+  const int64_t waves_total = (int64_t)gridDim.x * (blockDim.x / kWave);
+  for (int64_t t0 = ((int64_t)blockIdx.x * (blockDim.x / kWave) + wave) * TPW; t0 < T_tok;
+       t0 += waves_total * TPW) {
+    float acc[TPW][ES];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+#pragma unroll
+      for (int e = 0; e < ES; ++e) acc[i][e] = 0.f;
+    for (int c = lane; c < nchunk; c += kWave) {
+      float xv[TPW][VN];
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        const int64_t t = t0 + i;
+        if (t < T_tok) {
+          Vec16<T>::load(x + t * d + (int64_t)c * VN, xv[i]);
+        } else {
+#pragma unroll
+          for (int v = 0; v < VN; ++v) xv[i][v] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < ES; ++e) {
+        if (e0 + e < E) {
+          float wv[VN];
+          Vec16<T>::load(wr + (int64_t)(e0 + e) * d + (int64_t)c * VN, wv);
+#pragma unroll
+          for (int i = 0; i < TPW; ++i)
+#pragma unroll
+            for (int v = 0; v < VN; ++v) acc[i][e] = fmaf(xv[i][v], wv[v], acc[i][e]);
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+      for (int i = 0; i < TPW; ++i)
+#pragma unroll
+        for (int e = 0; e < ES; ++e) acc[i][e] += __shfl_xor(acc[i][e], off, kWave);
+    if (lane == 0) {
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        const int64_t t = t0 + i;
+        if (t < T_tok) {
+#pragma unroll
+          for (int e = 0; e < ES; ++e)
+            if (e0 + e < E) logits[t * E + e0 + e] = acc[i][e];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- top-k
+// One wave per token.  Lane l owns experts l, l+64, l+128, l+192.
+// `add_bias` adds b_router to the logits read (raw GEMM output) and, if
+// logits_out is set, writes the final logits back.
+__global__ void __launch_bounds__(256) topk_kernel(
+    const float* __restrict__ logits_in, const float* __restrict__ b_router,
+    const float* __restrict__ b_select, float* __restrict__ logits_out, int32_t* __restrict__ ids,
+    float* __restrict__ weights, int64_t T_tok, int E, int k, int score, int renorm) {
+  constexpr int PER = MOE_MAX_EXPERTS / kWave;  // 4
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int64_t waves_total = (int64_t)gridDim.x * (blockDim.x / kWave);
+  for (int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) + wave; t < T_tok;
+       t += waves_total) {
+    float L[PER], key[PER], sc[PER];
+    bool taken[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = lane + i * kWave;
+      taken[i] = e >= E;
+      L[i] = -INFINITY;
+      key[i] = -INFINITY;
+      sc[i] = 0.f;
+      if (e < E) {
+        L[i] = logits_in[t * E + e] + (b_router ? b_router[e] : 0.f);
+        if (logits_out) logits_out[t * E + e] = L[i];
+        if (score == MOE_SIGMOID) {
+          sc[i] = sigmoid_f32_via_f64(L[i]);
+          key[i] = b_select ? sc[i] + b_select[e] : sc[i];
+        } else {
+          key[i] = L[i];
+        }
+      }
+    }
+    int sel_e = -1;      // lane j < k keeps the j-th selection
+    float sel_v = 0.f;   // its logit (softmax) or sigmoid score
+    float first_logit = 0.f;
+    for (int j = 0; j < k; ++j) {
+      float bk = -INFINITY;
+      int bi = 0x7fffffff;
+      float bv = 0.f;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int e = lane + i * kWave;
+        if (!taken[i] && key_better(key[i], e, bk, bi)) {
+          bk = key[i];
+          bi = e;
+          bv = (score == MOE_SIGMOID) ? sc[i] : L[i];
+        }
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ok = __shfl_xor(bk, off, kWave);
+        const int oi = __shfl_xor(bi, off, kWave);
+        const float ov = __shfl_xor(bv, off, kWave);
+        if (key_better(ok, oi, bk, bi)) {
+          bk = ok;
+          bi = oi;
+          bv = ov;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (lane + i * kWave == bi) taken[i] = true;
+      if (lane == j) {
+        sel_e = bi;
+        sel_v = bv;
+      }
+      if (j == 0) first_logit = bv;
+    }
+    // weights
+    float num = 0.f;
+    float denom;
+    if (score == MOE_SOFTMAX) {
+      // the top key is the largest logit: use it as the softmax shift
+      num = (lane < k) ? __expf(sel_v - first_logit) : 0.f;
+      if (renorm) {
+        denom = num;
+      } else {
+        denom = 0.f;
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+          if (lane + i * kWave < E) denom += __expf(L[i] - first_logit);
+      }
+    } else {
+      num = (lane < k) ? sel_v : 0.f;
+      denom = num;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) denom += __shfl_xor(denom, off, kWave);
+    if (score == MOE_SIGMOID && !renorm) denom = 1.f;
+    if (lane < k) {
+      ids[t * k + lane] = sel_e;
+      weights[t * k + lane] = num / denom;
+    }
+  }
+}
+
+int grid_for(int64_t units, int per_block) {
+  const int64_t want = (units + per_block - 1) / per_block;
+  const int64_t cap = (int64_t)device_info().cus * 8;
+  return (int)(want < 1 ? 1 : (want > cap ? cap : want));
+}
+
+bool small_route_fits(const moe_route_args* a) {
+  const size_t es = a->act_dtype == MOE_F32 ? 4 : 2;
+  return a->E <= 8 && (size_t)a->E * a->d * es <= 64 * 1024;
+}
+
+bool mfma_route(const moe_route_args* a) {
+  return a->act_dtype == MOE_BF16 && a->E % 64 == 0 && a->d % 128 == 0 && !small_route_fits(a);
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" size_t moe_route_workspace_bytes(const moe_route_args* a) {
+  if (!a || a->x == nullptr || small_route_fits(a)) return 0;
+  return align_up((size_t)a->T * a->E * sizeof(float), 256);
+}
+
+extern "C" moe_status moe_route(const moe_route_args* a, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  clear_error();
+  MOE_CHECK_ARG(a != nullptr, "null args");
+  MOE_CHECK_ARG(a->T >= 0, "T < 0");
+  MOE_CHECK_ARG(a->E >= 1 && a->E <= MOE_MAX_EXPERTS, "E out of range [1, 256]");
+  MOE_CHECK_ARG(a->k >= 1 && a->k <= MOE_MAX_TOPK && a->k <= a->E, "k out of range [1, min(8, E)]");
+  MOE_CHECK_ARG(a->score == MOE_SOFTMAX || a->score == MOE_SIGMOID, "bad score");
+  MOE_CHECK_ARG(a->b_select == nullptr || a->score == MOE_SIGMOID,
+                "b_select needs sigmoid scores");
+  MOE_CHECK_ARG(a->act_dtype == MOE_F32 || a->act_dtype == MOE_BF16, "bad act_dtype");
+  MOE_CHECK_ARG(a->ids && a->weights, "ids/weights are required");
+  MOE_CHECK_ARG(aligned16(a->ids) && aligned16(a->weights), "ids/weights not 16-byte aligned");
+  if (a->T == 0) return MOE_OK;
+  const int tb = 256;
+  if (a->x == nullptr) {
+    MOE_CHECK_ARG(a->logits != nullptr, "x == NULL needs input logits");
+    MOE_CHECK_ARG(a->b_router == nullptr, "x == NULL: logits are final, b_router must be NULL");
+    topk_kernel<<<grid_for(a->T, 4), tb, 0, stream>>>(a->logits, nullptr, a->b_select, nullptr,
+                                                       a->ids, a->weights, a->T, a->E, a->k,
+                                                       a->score, a->renorm);
+    MOE_CHECK_LAUNCH();
+    return MOE_OK;
+  }
+  MOE_CHECK_ARG(a->w_router != nullptr, "w_router is required");
+  MOE_CHECK_ARG(a->d >= 1, "d < 1");
+  const int vn = a->act_dtype == MOE_F32 ? 4 : 8;
+  MOE_CHECK_ARG(a->d % vn == 0, "d must be a multiple of 16 bytes");
+  MOE_CHECK_ARG(aligned16(a->x) && aligned16(a->w_router), "x/w_router not 16-byte aligned");
+  if (small_route_fits(a)) {
+    constexpr int TPW = 4;
+    const size_t lds = (size_t)a->E * a->d * (a->act_dtype == MOE_F32 ? 4 : 2);
+    const int grid = grid_for(a->T, 4 * TPW);
+    if (a->act_dtype == MOE_F32) {
+      route_small_kernel<float, TPW><<<grid, tb, lds, stream>>>(
+          (const float*)a->x, (const float*)a->w_router, a->b_router, a->b_select, a->logits,
+          a->ids, a->weights, a->T, a->d, a->E, a->k, a->score, a->renorm);
+    } else {
+      route_small_kernel<bf16_t, TPW><<<grid, tb, lds, stream>>>(
+          (const bf16_t*)a->x, (const bf16_t*)a->w_router, a->b_router, a->b_select, a->logits,
+          a->ids, a->weights, a->T, a->d, a->E, a->k, a->score, a->renorm);
+    }
+    MOE_CHECK_LAUNCH();
+    return MOE_OK;
+  }
+  const size_t need = moe_route_workspace_bytes(a);
+  if (ws_bytes < need || (need && ws == nullptr)) {
+    set_error("moe_route: workspace too small");
+    return MOE_ERR_WORKSPACE;
+  }
+  float* raw = static_cast<float*>(ws);
+  if (mfma_route(a)) {
+    const moe_status st = dense_logits_gemm(a->x, a->w_router, raw, a->T, a->d, a->E, stream);
+    if (st != MOE_OK) return st;
+  } else {
+    constexpr int TPW = 4;
+    dim3 grid(grid_for(a->T, 4 * TPW), (a->E + 7) / 8);
+    if (a->act_dtype == MOE_F32) {
+      logits_valu_kernel<float, TPW><<<grid, tb, 0, stream>>>(
+          (const float*)a->x, (const float*)a->w_router, raw, a->T, a->d, a->E);
+    } else {
+      logits_valu_kernel<bf16_t, TPW><<<grid, tb, 0, stream>>>(
+          (const bf16_t*)a->x, (const bf16_t*)a->w_router, raw, a->T, a->d, a->E);
+    }
+    MOE_CHECK_LAUNCH();
+  }
+  topk_kernel<<<grid_for(a->T, 4), tb, 0, stream>>>(raw, a->b_router, a->b_select, a->logits,
+                                                     a->ids, a->weights, a->T, a->E, a->k,
+                                                     a->score, a->renorm);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}

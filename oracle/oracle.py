@@ -301,20 +301,29 @@ def ffn(rows64: np.ndarray, act: str, w1, w3, w2) -> np.ndarray:
     return a @ w2.T
 
 
-def expert_weights64(wl, local: int):
-    """fp64 weights of executed expert ``local`` (0-based within the rank)."""
+def expert_weights64(wl, local: int, cache: dict = None):
+    """fp64 weights of executed expert ``local`` (0-based within the rank).
+    ``cache`` (optional dict) keeps decoded experts for repeated use."""
+    if cache is not None and local in cache:
+        return cache[local]
     s = lambda nm: getattr(wl, nm)[local] if getattr(wl, nm) is not None else None
     w1 = to_f64(wl.w1[local], wl.w_dtype, s("s1"))
     w3 = to_f64(wl.w3[local], wl.w_dtype, s("s3")) if wl.act == "swiglu" else None
     w2 = to_f64(wl.w2[local], wl.w_dtype, s("s2"))
+    if cache is not None:
+        cache[local] = (w1, w3, w2)
     return w1, w3, w2
 
 
-def shared_weights64(wl):
+def shared_weights64(wl, cache: dict = None):
+    if cache is not None and "shared" in cache:
+        return cache["shared"]
     sh = wl.shared
     w1 = to_f64(sh["w1"], wl.w_dtype, sh.get("s1"))
     w3 = to_f64(sh["w3"], wl.w_dtype, sh.get("s3")) if wl.act == "swiglu" else None
     w2 = to_f64(sh["w2"], wl.w_dtype, sh.get("s2"))
+    if cache is not None:
+        cache["shared"] = (w1, w3, w2)
     return w1, w3, w2
 
 
@@ -384,7 +393,7 @@ def layer(wl, cf=None, logits32=None, ids_override=None, with_ffn=True) -> dict:
     return out
 
 
-def token_outputs(wl, tokens, ids, weights, slot, with_shared=True) -> np.ndarray:
+def token_outputs(wl, tokens, ids, weights, slot, with_shared=True, cache=None) -> np.ndarray:
     """Second formulation, no permutation: for each listed token,
     y[t] = x[t] (+ shared(x[t])) + sum_j w[t,j] FFN_{ids[t,j]}(x[t]) over the
     kept (slot >= 0) executed assignments.  Used for sampled checks at full
@@ -393,13 +402,13 @@ def token_outputs(wl, tokens, ids, weights, slot, with_shared=True) -> np.ndarra
     x64 = to_f64(wl.x[tokens], wl.act_dtype)
     y = x64.copy()
     if wl.shared is not None and with_shared:
-        y += ffn(x64, wl.act, *shared_weights64(wl))
+        y += ffn(x64, wl.act, *shared_weights64(wl, cache))
     for e in range(wl.e_begin, wl.e_end):
         hit = [(i, j) for i, t in enumerate(tokens) for j in range(ids.shape[1])
                if ids[t, j] == e and slot[t, j] >= 0]
         if not hit:
             continue
-        w1, w3, w2 = expert_weights64(wl, e - wl.e_begin)
+        w1, w3, w2 = expert_weights64(wl, e - wl.e_begin, cache)
         ii = np.array([i for i, _ in hit])
         jj = np.array([j for _, j in hit])
         out = ffn(x64[ii], wl.act, w1, w3, w2)
@@ -407,9 +416,9 @@ def token_outputs(wl, tokens, ids, weights, slot, with_shared=True) -> np.ndarra
     return y
 
 
-def expert_rows(wl, rows_x64: np.ndarray, e: int) -> np.ndarray:
+def expert_rows(wl, rows_x64: np.ndarray, e: int, cache=None) -> np.ndarray:
     """FFN of executed expert e on the given rows (for sampled Ys checks)."""
-    w1, w3, w2 = expert_weights64(wl, e - wl.e_begin)
+    w1, w3, w2 = expert_weights64(wl, e - wl.e_begin, cache)
     return ffn(rows_x64, wl.act, w1, w3, w2)
 
 
@@ -424,3 +433,8 @@ def rowmax_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     den = np.abs(ref).max(axis=1)
     den = np.where(den > 0, den, 1.0)
     return float((num / den).max())
+
+
+def shared_rows(wl, rows_x64: np.ndarray, cache=None) -> np.ndarray:
+    """Shared-expert FFN on the given rows."""
+    return ffn(rows_x64, wl.act, *shared_weights64(wl, cache))

@@ -143,6 +143,8 @@ def make_workload(cfg: int, **over) -> Workload:
     k, R, e_begin, e_end, cf, seed, offset, select_bias).  Overrides keep the
     value distributions and draw order of the named config."""
     c = dict(CONFIGS[cfg])
+    if "E" in over and "e_end" not in over:
+        c["e_end"] = min(c["e_end"], over["E"])
     c.update(over)
     T, d, E, k, h = c["T"], c["d"], c["E"], c["k"], c["h"]
     wl = Workload(cfg=cfg, name=c["name"], T=T, d=d, E=E, k=k, R=c["R"], h=h,
