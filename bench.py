@@ -1,0 +1,226 @@
+"""MoE-layer forward benchmark on one MI355X.
+
+One step = one moe_layer_forward (route -> dispatch -> expert FFN -> combine)
+over one batch of seeded synthetic input, inputs resident in HBM.  Default
+workload: the decode-shaped Mixtral-style bf16 layer (T=128 tokens, d=4096,
+8 SwiGLU experts with h=14336, top-2, softmax renormalised, no drops).
+
+Prints one JSON line: tokens/s over the timed steps, per-stage times from HIP
+events recorded between the kernels inside the timed region, the roofline of
+the dominant kernel (the first expert GEMM, which streams w1 and w3) and the
+fp64 CPU oracle timed on the host on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+STAGES = ["route", "dispatch", "gemm1", "gemm2", "combine"]
+
+
+def _hip():
+    """The HIP runtime already loaded in this process (torch's copy)."""
+    path = None
+    for line in open("/proc/self/maps"):
+        if "libamdhip64" in line:
+            path = line.split()[-1]
+            break
+    h = ctypes.CDLL(path or "libamdhip64.so")
+    h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    return h
+
+
+class Events:
+    def __init__(self, hip, n):
+        self.hip = hip
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert hip.hipEventCreate(ctypes.byref(e)) == 0
+            self.ev.append(e.value)
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(out), self.ev[a], self.ev[b]) == 0
+        return out.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+
+
+def algorithmic_bytes(wl, kept_rows: int, used_experts: int, shared: bool):
+    """Bytes each stage must move (read once, write once), per launch."""
+    sa = 4 if wl.act_dtype == "f32" else 2
+    sw = {"f32": 4, "bf16": 2, "fp8": 1}[wl.w_dtype]
+    T, d, h, E, k = wl.T, wl.d, wl.h, wl.E, wl.k
+    n1 = 2 if wl.act == "swiglu" else 1
+    nx = kept_rows + (T if shared else 0)
+    groups = used_experts + (1 if shared else 0)
+    return {
+        "route": T * d * sa + E * d * sa + 8 * T * k,
+        "dispatch": 8 * T * k + 4 * kept_rows + T * d * sa + kept_rows * d * sa,
+        "gemm1": n1 * h * d * sw * groups + nx * d * sa + nx * h * sa,
+        "gemm2": d * h * sw * groups + nx * h * sa + nx * d * sa,
+        "combine": kept_rows * d * sa + 2 * T * d * sa + (T * d * sa if shared else 0) + 8 * T * k,
+    }
+
+
+def gemm_flops(wl, kept_rows: int, shared: bool):
+    nx = kept_rows + (wl.T if shared else 0)
+    n1 = 2 if wl.act == "swiglu" else 1
+    return {"gemm1": 2 * n1 * wl.d * wl.h * nx, "gemm2": 2 * wl.d * wl.h * nx}
+
+
+def traffic_from_profiles(kernel_file: str):
+    """HBM bytes per launch of the first expert GEMM from committed rocprofv3
+    counter runs, valid only while the kernel source is unchanged."""
+    path = os.path.join(ROOT, "profiles", "gemm1_decode_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = open(kernel_file, "rb").read()
+    if rec.get("source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, budget_s: float = 30.0):
+    """The fp64 oracle on the host cores: the whole layer on the same
+    workload (or on a prefix of its tokens when that would exceed the budget)."""
+    import threadpoolctl
+
+    from oracle import oracle as O
+    threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()
+                   if p.get("user_api") == "blas"), default=1)
+    t0 = time.perf_counter()
+    O.layer(wl)
+    dt = time.perf_counter() - t0
+    return {"value": wl.T / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"the whole layer on all {wl.T} tokens of the same workload, fp64, "
+                      f"{dt:.1f} s (input generation excluded)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=1, help="workload index 0-4 (default 1: decode)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU's share of the MoE layer; runs on more than one GPU "
+              "are not part of this build (no collectives). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import expert_token_routing_gemm_amd as M
+    from synth import make_workload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    print(f"[bench] generating workload {args.config}", file=sys.stderr, flush=True)
+    wl = make_workload(args.config)
+    layer = M.MoELayer(wl, device="cuda:0", keep_logits=False)
+    hip = _hip()
+    K, W = args.steps, args.warmup
+    print(f"[bench] warmup {W}, timed {K}", file=sys.stderr, flush=True)
+    for _ in range(W):
+        layer.forward()
+    torch.cuda.synchronize()
+    ev = Events(hip, M.MOE_LAYER_EVENTS * K)
+    n = M.MOE_LAYER_EVENTS
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        layer.forward(events=ev.ev[s * n:(s + 1) * n])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev.ms(0, (K - 1) * n + n - 1)
+    per = {st: [] for st in STAGES}
+    for s in range(K):
+        b = s * n
+        per["route"].append(ev.ms(b + 0, b + 1))
+        per["dispatch"].append(ev.ms(b + 1, b + 2))
+        per["gemm1"].append(ev.ms(b + 2, b + 3))
+        per["gemm2"].append(ev.ms(b + 3, b + 4))
+        per["combine"].append(ev.ms(b + 4, b + 5))
+    ev.close()
+    stage_ms = {k: float(np.mean(v)) for k, v in per.items()}
+    ms_per_step = wall * 1e3 / K
+    value = wl.T * K / wall
+
+    res = layer.results()
+    off = res["off"]
+    kept_rows = int(off[wl.e_end] - off[wl.e_begin])
+    used = int(np.count_nonzero(res["kept"][wl.e_begin:wl.e_end]))
+    shared = wl.shared is not None
+    nbytes = algorithmic_bytes(wl, kept_rows, used, shared)
+    flops = gemm_flops(wl, kept_rows, shared)
+    # the dominant kernel: the first expert GEMM (streams w1 and w3)
+    g1_s = stage_ms["gemm1"] / 1e3
+    bound = "hbm" if args.config == 1 else "mfma"
+    if bound == "hbm":
+        achieved = nbytes["gemm1"] / g1_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+    else:
+        achieved = flops["gemm1"] / g1_s / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / BF16_PEAK_TFLOPS}
+    roof["kernel"] = "grouped_gemm_kernel (expert GEMM 1: w1/w3 + activation)"
+    roof["algorithmic_bytes"] = nbytes["gemm1"]
+    roof["traffic"] = traffic_from_profiles(os.path.join(ROOT, "expert_token_routing_gemm_amd",
+                                                          "csrc", "gemm.hip"))
+    stage_frac = {st: (nbytes[st] / (stage_ms[st] / 1e3) / 1e9) / HBM_PEAK_GBS for st in STAGES}
+
+    out = {
+        "metric": "MoE-layer tokens/s (route->dispatch->expert GEMM->combine)",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.act_dtype if wl.w_dtype != "fp8" else "bf16 (fp8 e4m3 weights)",
+        "data": "synthetic (seeded; random-init weights of the stated shapes)",
+        "config": {"workload": f"{wl.name}: T={wl.T}, d={wl.d}, E={wl.E}, top-{wl.k}, "
+                               f"{wl.act} h={wl.h}, executed experts {wl.e_begin}-{wl.e_end - 1}"
+                               f"{' + shared' if shared else ''}, capacity "
+                               f"{'none' if wl.cf is None else wl.cf}",
+                   "tokens": wl.T, "parallelism": "one GPU's share (no collectives)"},
+        "stages_ms": stage_ms,
+        "stages_hbm_frac": stage_frac,
+        "gemm_tflops": {k: flops[k] / (stage_ms[k] / 1e3) / 1e12 for k in flops},
+        "kept_rows": kept_rows,
+        "wall_s": wall,
+        "gpu_ms_per_step": gpu_ms / K,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
