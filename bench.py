@@ -114,6 +114,31 @@ def cpu_baseline(wl, budget_s: float = 30.0):
                       f"{dt:.1f} s (input generation excluded)"}
 
 
+def copy_probe(mib: int, steps: int):
+    """A plain copy of known size (and a read-only reduction) on the device:
+    the reference for scaling the rocprofv3 byte counters and the measured
+    ceiling of HBM bandwidth on this machine."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    out = {}
+    for name, fn, nbytes in (("copy", lambda: dst.copy_(src), 2 * n * 4),
+                             ("read", lambda: src.sum(), n * 4)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        out[name] = {"bytes_per_launch": nbytes, "ms": ms, "GBps": nbytes / ms / 1e6}
+    print(json.dumps({"copy_probe_mib": mib, **out}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,6 +146,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1, help="workload index 0-4 (default 1: decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="instead of the layer: time a plain device copy of MIB MiB (HBM "
+                         "calibration for the traffic counters) and a full read (sum)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU's share of the MoE layer; runs on more than one GPU "
@@ -135,6 +163,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        copy_probe(args.copy_probe, args.steps)
+        return
     print(f"[bench] generating workload {args.config}", file=sys.stderr, flush=True)
     wl = make_workload(args.config)
     layer = M.MoELayer(wl, device="cuda:0", keep_logits=False)

@@ -53,7 +53,7 @@ struct Row16<bf16_t> {
   }
 };
 
-template <typename ET, int UNROLL>
+template <typename ET, int UNROLL, int WPT>
 __global__ void __launch_bounds__(kThreads) combine_kernel(
     const uint4* __restrict__ x, const uint4* __restrict__ shared_out,
     const uint4* __restrict__ y_send, const int32_t* __restrict__ ids,
@@ -61,8 +61,12 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(
     int64_t T, int k, int e_begin, int e_end, int row16) {
   constexpr int N = Row16<ET>::N;
   const int lane = lane_id();
-  const int64_t waves = (int64_t)gridDim.x * (kThreads / 64);
-  for (int64_t t = (int64_t)blockIdx.x * (kThreads / 64) + threadIdx.x / 64; t < T; t += waves) {
+  // WPT waves share one token's row (decode-sized batches); the row's 16-byte
+  // pieces are dealt round-robin over their 64*WPT lanes.
+  const int64_t slots = (int64_t)gridDim.x * (kThreads / 64);
+  const int64_t wid = (int64_t)blockIdx.x * (kThreads / 64) + threadIdx.x / 64;
+  const int sub = (int)(wid % WPT);
+  for (int64_t t = wid / WPT; t < T; t += slots / WPT) {
     int sj[MOE_MAX_TOPK];  // -1: nothing to add for choice j
     float wj[MOE_MAX_TOPK];
     bool any = false;
@@ -83,17 +87,18 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(
     const uint4* xr = x + t * row16;
     const uint4* sr = shared_out ? shared_out + t * row16 : nullptr;
     uint4* yr = y + t * row16;
-    for (int c0 = lane; c0 < row16; c0 += 64 * UNROLL) {
+    constexpr int STRIDE = 64 * WPT;
+    for (int c0 = sub * 64 + lane; c0 < row16; c0 += STRIDE * UNROLL) {
       uint4 xv[UNROLL];
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
-        const int c = c0 + u * 64;
+        const int c = c0 + u * STRIDE;
         xv[u] = (c < row16) ? xr[c] : uint4{0, 0, 0, 0};
       }
       if (!any && !sr) {
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
-          const int c = c0 + u * 64;
+          const int c = c0 + u * STRIDE;
           if (c < row16) yr[c] = xv[u];
         }
         continue;
@@ -104,7 +109,7 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(
       if (sr) {
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
-          const int c = c0 + u * 64;
+          const int c = c0 + u * STRIDE;
           if (c < row16) {
             float f[N];
             Row16<ET>::to_f32(sr[c], f);
@@ -121,7 +126,7 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(
         uint4 ev[UNROLL];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
-          const int c = c0 + u * 64;
+          const int c = c0 + u * STRIDE;
           ev[u] = (c < row16) ? er[c] : uint4{0, 0, 0, 0};
         }
 #pragma unroll
@@ -134,7 +139,7 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(
       }
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
-        const int c = c0 + u * 64;
+        const int c = c0 + u * STRIDE;
         if (c < row16) yr[c] = Row16<ET>::from_f32(acc[u]);
       }
     }
@@ -163,17 +168,29 @@ extern "C" moe_status moe_combine(const moe_combine_args* a, hipStream_t stream)
                 "rows not 16-byte aligned");
   MOE_CHECK_ARG(a->x != a->y, "y may not alias x");
   const int row16 = (int)((int64_t)a->d * es / 16);
-  const int64_t want = (a->T + 3) / 4;
+  // decode-sized batches: a workgroup per token so every load is in flight at once
+  const bool wide = a->T < 4 * (int64_t)device_info().cus;
+  const int64_t want = wide ? a->T : (a->T + 3) / 4;
   const int64_t cap = (int64_t)device_info().cus * 16;
   const int grid = (int)(want < cap ? want : cap);
   if (a->act_dtype == MOE_F32) {
-    combine_kernel<float, 2><<<grid, kThreads, 0, stream>>>(
-        (const uint4*)a->x, (const uint4*)a->shared_out, (const uint4*)a->y_send, a->ids, a->slot,
-        a->weights, (uint4*)a->y, a->T, a->k, a->e_begin, a->e_end, row16);
+    if (wide)
+      combine_kernel<float, 2, 4><<<grid, kThreads, 0, stream>>>(
+          (const uint4*)a->x, (const uint4*)a->shared_out, (const uint4*)a->y_send, a->ids, a->slot,
+          a->weights, (uint4*)a->y, a->T, a->k, a->e_begin, a->e_end, row16);
+    else
+      combine_kernel<float, 4, 1><<<grid, kThreads, 0, stream>>>(
+          (const uint4*)a->x, (const uint4*)a->shared_out, (const uint4*)a->y_send, a->ids, a->slot,
+          a->weights, (uint4*)a->y, a->T, a->k, a->e_begin, a->e_end, row16);
   } else {
-    combine_kernel<bf16_t, 2><<<grid, kThreads, 0, stream>>>(
-        (const uint4*)a->x, (const uint4*)a->shared_out, (const uint4*)a->y_send, a->ids, a->slot,
-        a->weights, (uint4*)a->y, a->T, a->k, a->e_begin, a->e_end, row16);
+    if (wide)
+      combine_kernel<bf16_t, 2, 4><<<grid, kThreads, 0, stream>>>(
+          (const uint4*)a->x, (const uint4*)a->shared_out, (const uint4*)a->y_send, a->ids, a->slot,
+          a->weights, (uint4*)a->y, a->T, a->k, a->e_begin, a->e_end, row16);
+    else
+      combine_kernel<bf16_t, 4, 1><<<grid, kThreads, 0, stream>>>(
+          (const uint4*)a->x, (const uint4*)a->shared_out, (const uint4*)a->y_send, a->ids, a->slot,
+          a->weights, (uint4*)a->y, a->T, a->k, a->e_begin, a->e_end, row16);
   }
   MOE_CHECK_LAUNCH();
   return MOE_OK;

@@ -75,6 +75,12 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t q) {
   return __uint_as_float(__float_as_uint(mag) | ((q & 0x80u) << 24));
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for
+// every outstanding global load (vmcnt(0)), which would drain register
+// prefetches issued just before it; here only the LDS counter is drained.
+// The "memory" clobber keeps the compiler from moving memory accesses across.
+#define MOE_BARRIER_LDS() asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
+
 // ---------------------------------------------------------------- wave ops
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 

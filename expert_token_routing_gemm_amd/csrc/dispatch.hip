@@ -196,6 +196,156 @@ __global__ void __launch_bounds__(kThreads) rank_pack_kernel(
   }
 }
 
+// ---------------------------------------------------------------- small batches
+// Decode-sized batches (T*k <= kSmallAssign): one workgroup does the
+// histogram, the offsets and the ranks (rounds of 16 waves x 64 assignments in
+// token-major order, a running per-expert position carried across rounds),
+// and pack_kernel copies the rows with one wave per token.  Two launches
+// instead of three, and no serial loop over many histogram blocks.
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallWaves = kSmallThreads / 64;
+constexpr int kSmallAssign = 4096;
+
+__global__ void __launch_bounds__(kSmallThreads) plan_small_kernel(
+    const int32_t* __restrict__ ids, int64_t n_assign, int k, int E, int R, int C,
+    int32_t* __restrict__ counts, int32_t* __restrict__ kept, int32_t* __restrict__ off,
+    int32_t* __restrict__ rank_counts, int32_t* __restrict__ rank_off,
+    int32_t* __restrict__ slot_out, int32_t* __restrict__ src_out) {
+  __shared__ int cnt[MOE_MAX_EXPERTS];
+  __shared__ int run[MOE_MAX_EXPERTS];
+  __shared__ int offs[MOE_MAX_EXPERTS + 1];
+  __shared__ int wc[kSmallWaves][MOE_MAX_EXPERTS];
+  __shared__ int wsum[kSmallWaves];
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int w = tid / 64;
+  for (int e = tid; e < MOE_MAX_EXPERTS; e += kSmallThreads) {
+    cnt[e] = 0;
+    run[e] = 0;
+  }
+  __syncthreads();
+  for (int64_t g = tid; g < n_assign; g += kSmallThreads) {
+    const int e = ids[g];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  // exclusive scan of kept over the experts (threads 0..255 = waves 0..3)
+  int kp = 0, incl = 0;
+  if (tid < MOE_MAX_EXPERTS) {
+    kp = tid < E ? min(cnt[tid], C) : 0;
+    incl = kp;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += u;
+    }
+    if (lane == 63) wsum[w] = incl;
+  }
+  __syncthreads();
+  if (tid < MOE_MAX_EXPERTS) {
+    for (int i = 0; i < w; ++i) incl += wsum[i];
+    if (tid < E) {
+      counts[tid] = cnt[tid];
+      kept[tid] = kp;
+      off[tid] = incl - kp;
+      offs[tid] = incl - kp;
+    }
+    if (tid == E - 1) {
+      off[E] = incl;
+      offs[E] = incl;
+    }
+  }
+  __syncthreads();
+  const int per = E / R;
+  for (int r = tid; r < R; r += kSmallThreads) {
+    rank_counts[r] = offs[(r + 1) * per] - offs[r * per];
+    rank_off[r] = offs[r * per];
+  }
+  if (tid == 0) rank_off[R] = offs[E];
+  // ranks, one round of kSmallThreads assignments at a time
+  for (int64_t base = 0; base < n_assign; base += kSmallThreads) {
+    for (int e = lane; e < MOE_MAX_EXPERTS; e += 64) wc[w][e] = 0;
+    __syncthreads();
+    const int64_t g = base + tid;
+    const bool in_range = g < n_assign;
+    const int e = in_range ? ids[g] : -1;
+    const bool valid = in_range && e >= 0 && e < E;
+    if (valid) atomicAdd(&wc[w][e], 1);
+    __syncthreads();
+    for (int ee = tid; ee < E; ee += kSmallThreads) {
+      int r = run[ee];
+#pragma unroll
+      for (int i = 0; i < kSmallWaves; ++i) {
+        const int c = wc[i][ee];
+        wc[i][ee] = r;
+        r += c;
+      }
+      run[ee] = r;
+    }
+    __syncthreads();
+    uint64_t todo = ballot(valid);
+    int rk = 0;
+    while (todo) {
+      const int leader = __ffsll((long long)todo) - 1;
+      const int el = __shfl(e, leader, 64);
+      const uint64_t m = ballot(valid && e == el);
+      if (valid && e == el) rk = popc64(m & lanemask_lt());
+      todo &= ~m;
+    }
+    if (in_range) {
+      int s = -1;
+      if (valid) {
+        const int pos = wc[w][e] + rk;
+        if (pos < C) {
+          s = offs[e] + pos;
+          src_out[s] = (int32_t)(g / k);
+        }
+      }
+      slot_out[g] = s;
+    }
+    __syncthreads();
+  }
+}
+
+// One workgroup per token (its 4 waves split the row): the row is read once
+// and written to each kept slot, with every piece in flight at once.
+template <int UNROLL>
+__global__ void __launch_bounds__(kThreads) pack_kernel(const int32_t* __restrict__ slot,
+                                                       const u32x4* __restrict__ x,
+                                                       u32x4* __restrict__ x_send, int64_t T, int k,
+                                                       int row16) {
+  const int lane = threadIdx.x;  // 0..255 over the row
+  const int64_t t = blockIdx.x;
+  if (t >= T) return;
+  int sj[MOE_MAX_TOPK];
+  bool any = false;
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    sj[j] = j < k ? slot[t * k + j] : -1;
+    any |= sj[j] >= 0;
+  }
+  if (!any) return;
+  const u32x4* xr = x + t * row16;
+  for (int c0 = lane; c0 < row16; c0 += kThreads * UNROLL) {
+    u32x4 v[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int c = c0 + u * kThreads;
+      if (c < row16) v[u] = xr[c];
+    }
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      if (sj[j] < 0) continue;
+      u32x4* dst = x_send + (int64_t)sj[j] * row16;
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const int c = c0 + u * kThreads;
+        if (c < row16) dst[c] = v[u];
+      }
+    }
+  }
+}
+
 struct Plan {
   int tokens_per_block;
   int nblocks;
@@ -224,7 +374,7 @@ extern "C" int64_t moe_send_rows_max(int64_t T, int32_t k, int32_t E, int32_t ca
 }
 
 extern "C" size_t moe_dispatch_workspace_bytes(const moe_dispatch_args* a) {
-  if (!a || a->T <= 0 || a->k <= 0) return 0;
+  if (!a || a->T <= 0 || a->k <= 0 || a->T * a->k <= kSmallAssign) return 0;
   const Plan p = plan_for(a->T, a->k);
   return align_up((size_t)p.nblocks * a->E * sizeof(int32_t), 256);
 }
@@ -249,9 +399,19 @@ extern "C" moe_status moe_dispatch(const moe_dispatch_args* a, void* ws, size_t 
   const int row16 = (int)((int64_t)a->d * es / 16);
   const Plan p = plan_for(a->T, a->k);
   const size_t need = moe_dispatch_workspace_bytes(a);
-  if (a->T > 0 && (ws_bytes < need || ws == nullptr)) {
+  if (need > 0 && (ws_bytes < need || ws == nullptr)) {
     set_error("moe_dispatch: workspace too small");
     return MOE_ERR_WORKSPACE;
+  }
+  if (a->T > 0 && a->T * a->k <= kSmallAssign) {
+    plan_small_kernel<<<1, kSmallThreads, 0, stream>>>(
+        a->ids, a->T * a->k, a->k, a->E, a->R, a->capacity, a->counts, a->kept, a->expert_off,
+        a->rank_counts, a->rank_off, a->slot, a->src);
+    MOE_CHECK_LAUNCH();
+    pack_kernel<2><<<(int)a->T, kThreads, 0, stream>>>(
+        a->slot, (const u32x4*)a->x, (u32x4*)a->x_send, a->T, a->k, row16);
+    MOE_CHECK_LAUNCH();
+    return MOE_OK;
   }
   int32_t* blk = static_cast<int32_t*>(ws);
   if (a->T > 0) {

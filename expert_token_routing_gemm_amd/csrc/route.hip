@@ -19,6 +19,8 @@
 // Large E (E % 64 == 0, bf16) computes the logits with the bf16 MFMA GEMM of
 // the expert FFN (router intensity 2E/s_a is 64-256 flop/B there, above the
 // VALU ridge), then runs topk_kernel.
+#include <algorithm>
+
 #include "common.h"
 #include "gemm.h"
 
@@ -144,7 +146,7 @@ __device__ void finish_token_small(const float* L, int E, int k, int score, int 
 // ---------------------------------------------------------------- E <= 8 fused
 // Block = 4 waves; each wave owns TPW tokens at a time.  Lane l covers the
 // 16-byte chunks l, l+64, ... of a row (coalesced 128-bit loads of x).
-template <typename T, int TPW>
+template <typename T, int TPW, bool WR_LDS>
 __global__ void __launch_bounds__(256) route_small_kernel(
     const T* __restrict__ x, const T* __restrict__ wr, const float* __restrict__ b_router,
     const float* __restrict__ b_select, float* __restrict__ logits_out, int32_t* __restrict__ ids,
@@ -152,14 +154,16 @@ __global__ void __launch_bounds__(256) route_small_kernel(
   constexpr int EMAX = 8;
   constexpr int VN = Vec16<T>::N;  // elements per 16 B
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  T* sw = reinterpret_cast<T*>(smem_raw);  // [E][d]
-  {
+  const T* sw = wr;  // [E][d]: LDS copy when staged, else read through L2
+  if constexpr (WR_LDS) {
+    T* dst = reinterpret_cast<T*>(smem_raw);
     const int n16 = E * d / VN;
     const uint4* g = reinterpret_cast<const uint4*>(wr);
-    uint4* s = reinterpret_cast<uint4*>(sw);
+    uint4* s = reinterpret_cast<uint4*>(dst);
     for (int i = threadIdx.x; i < n16; i += blockDim.x) s[i] = g[i];
+    __syncthreads();
+    sw = dst;
   }
-  __syncthreads();
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
   const int nchunk = d / VN;  // 16-byte chunks per row
@@ -220,6 +224,63 @@ __global__ void __launch_bounds__(256) route_small_kernel(
         finish_token_small<EMAX>(L, E, k, score, renorm, b_select, t, ids, weights);
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------- decode-sized T
+// One workgroup per token: the 4 waves split the row, so every lane has only
+// a couple of 16-byte pieces of x (and of each W_r row, read through L2) to
+// fetch and all of them are in flight at once; the partial logits are
+// reduced across lanes by shuffles and across waves through LDS.
+template <typename T>
+__global__ void __launch_bounds__(256) route_decode_kernel(
+    const T* __restrict__ x, const T* __restrict__ wr, const float* __restrict__ b_router,
+    const float* __restrict__ b_select, float* __restrict__ logits_out, int32_t* __restrict__ ids,
+    float* __restrict__ weights, int64_t T_tok, int d, int E, int k, int score, int renorm) {
+  constexpr int EMAX = 8;
+  constexpr int VN = Vec16<T>::N;
+  __shared__ float part[4][EMAX];
+  const int64_t t = blockIdx.x;
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int nchunk = d / VN;
+  float acc[EMAX];
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) acc[e] = 0.f;
+#pragma unroll 2
+  for (int c = threadIdx.x; c < nchunk; c += 256) {
+    float xv[VN];
+    Vec16<T>::load(x + t * d + (int64_t)c * VN, xv);
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) {
+      if (e < E) {
+        float wv[VN];
+        Vec16<T>::load(wr + (int64_t)e * d + (int64_t)c * VN, wv);
+#pragma unroll
+        for (int v = 0; v < VN; ++v) acc[e] = fmaf(xv[v], wv[v], acc[e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) acc[e] += __shfl_xor(acc[e], off, kWave);
+  if (lane == 0) {
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) part[wave][e] = acc[e];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float L[EMAX];
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e)
+      L[e] = (e < E) ? (part[0][e] + part[1][e]) + (part[2][e] + part[3][e]) +
+                           (b_router ? b_router[e] : 0.f)
+                     : 0.f;
+    if (logits_out) {
+      for (int e = 0; e < E; ++e) logits_out[t * E + e] = L[e];
+    }
+    finish_token_small<EMAX>(L, E, k, score, renorm, b_select, t, ids, weights);
   }
 }
 
@@ -441,17 +502,34 @@ extern "C" moe_status moe_route(const moe_route_args* a, void* ws, size_t ws_byt
   MOE_CHECK_ARG(a->d % vn == 0, "d must be a multiple of 16 bytes");
   MOE_CHECK_ARG(aligned16(a->x) && aligned16(a->w_router), "x/w_router not 16-byte aligned");
   if (small_route_fits(a)) {
-    constexpr int TPW = 4;
-    const size_t lds = (size_t)a->E * a->d * (a->act_dtype == MOE_F32 ? 4 : 2);
-    const int grid = grid_for(a->T, 4 * TPW);
-    if (a->act_dtype == MOE_F32) {
-      route_small_kernel<float, TPW><<<grid, tb, lds, stream>>>(
-          (const float*)a->x, (const float*)a->w_router, a->b_router, a->b_select, a->logits,
-          a->ids, a->weights, a->T, a->d, a->E, a->k, a->score, a->renorm);
+    // Many tokens: stage W_r in LDS once per workgroup and loop over tokens.
+    // Few tokens (decode): one workgroup per token, W_r read through L2.
+    const bool stage = a->T > 1024;
+    const size_t lds = stage ? (size_t)a->E * a->d * (a->act_dtype == MOE_F32 ? 4 : 2) : 0;
+    if (stage) {
+      constexpr int TPW = 4;
+      const int grid = (int)std::min<int64_t>((a->T + 4 * TPW - 1) / (4 * TPW),
+                                              (int64_t)device_info().cus * 2);
+      if (a->act_dtype == MOE_F32) {
+        route_small_kernel<float, TPW, true><<<grid, tb, lds, stream>>>(
+            (const float*)a->x, (const float*)a->w_router, a->b_router, a->b_select, a->logits,
+            a->ids, a->weights, a->T, a->d, a->E, a->k, a->score, a->renorm);
+      } else {
+        route_small_kernel<bf16_t, TPW, true><<<grid, tb, lds, stream>>>(
+            (const bf16_t*)a->x, (const bf16_t*)a->w_router, a->b_router, a->b_select, a->logits,
+            a->ids, a->weights, a->T, a->d, a->E, a->k, a->score, a->renorm);
+      }
     } else {
-      route_small_kernel<bf16_t, TPW><<<grid, tb, lds, stream>>>(
-          (const bf16_t*)a->x, (const bf16_t*)a->w_router, a->b_router, a->b_select, a->logits,
-          a->ids, a->weights, a->T, a->d, a->E, a->k, a->score, a->renorm);
+      const int grid = (int)a->T;
+      if (a->act_dtype == MOE_F32) {
+        route_decode_kernel<float><<<grid, tb, 0, stream>>>(
+            (const float*)a->x, (const float*)a->w_router, a->b_router, a->b_select, a->logits,
+            a->ids, a->weights, a->T, a->d, a->E, a->k, a->score, a->renorm);
+      } else {
+        route_decode_kernel<bf16_t><<<grid, tb, 0, stream>>>(
+            (const bf16_t*)a->x, (const bf16_t*)a->w_router, a->b_router, a->b_select, a->logits,
+            a->ids, a->weights, a->T, a->d, a->E, a->k, a->score, a->renorm);
+      }
     }
     MOE_CHECK_LAUNCH();
     return MOE_OK;

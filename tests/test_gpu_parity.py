@@ -122,6 +122,9 @@ SMALL = {
     "c2-small": (2, dict(T=1000, d=512, h=640)),
     "c3-small": (3, dict(T=4096, d=256, h=512)),
     "c4-small": (4, dict(T=256, d=512, h=256)),
+    # just above the single-workgroup dispatch limit (T*k > 4096): multi-block path
+    "c2-multiblock-dispatch": (2, dict(T=2100, d=256, h=384)),
+    "c4-multiblock-dispatch": (4, dict(T=600, d=256, h=256)),
 }
 
 
