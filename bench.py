@@ -215,10 +215,11 @@ def main():
         achieved = flops["gemm1"] / g1_s / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / BF16_PEAK_TFLOPS}
-    roof["kernel"] = "grouped_gemm_kernel (expert GEMM 1: w1/w3 + activation)"
+    roof["kernel"] = ("stream_gemm_kernel" if args.config == 1 else "grouped_gemm_kernel") + \
+        " (expert GEMM 1: w1/w3 + activation)"
     roof["algorithmic_bytes"] = nbytes["gemm1"]
     roof["traffic"] = traffic_from_profiles(os.path.join(ROOT, "expert_token_routing_gemm_amd",
-                                                          "csrc", "gemm.hip"))
+                                                          "csrc", "stream_gemm.hip"))
     stage_frac = {st: (nbytes[st] / (stage_ms[st] / 1e3) / 1e9) / HBM_PEAK_GBS for st in STAGES}
 
     out = {

@@ -1,0 +1,346 @@
+// Grouped expert GEMM for many-row bf16 groups (prefill), gfx950.
+//
+// Local expert compute (Ultralytics glossary "Expert Parallelism", "How
+// Tokens Move Between GPUs", step 3): each executed expert multiplies its
+// gathered rows by its own weights, independently of the others.
+//
+// Design (MI355X-specific):
+//  * 256x256 output tile per workgroup of 8 waves (2 per SIMD); each wave
+//    owns 128x64 as 4x2 v_mfma_f32_32x32x16_bf16 subtiles (the full-rate bf16
+//    MFMA on gfx950; 128 fp32 accumulators per lane in AGPRs).  Per k the
+//    workgroup reads 8*(128+64)*2 bytes of LDS and writes 512*2 by DMA for
+//    2*256*256 flops, about 0.03 B/flop: within LDS bandwidth at the MFMA
+//    peak, where 64x64 wave tiles are not.  Groups of a few hundred rows use
+//    128x256 tiles (4 waves of 128x64) to pad less.
+//  * Global -> LDS with global_load_lds_dwordx4 (no register staging): a
+//    4-stage ring of 32-k stages (32 KB each), filled three stages ahead;
+//    each wave waits for its own loads of a stage (vmcnt), then one
+//    workgroup barrier makes them visible.  The compiler does not track
+//    these waits, they are issued explicitly.
+//  * Every wave instruction fills 1 KB of LDS = 16 tile rows x 64 bytes.
+//    Inside a 1 KB block the four 16-byte chunks of row r are stored XOR-
+//    swizzled by h(r) = ((r >> 1) ^ (r >> 2)) & 3, so the MFMA fragment reads
+//    (consecutive rows, same chunk) hit distinct banks for 8- and 16-lane
+//    groups.
+//  * Persistent grid with the same device-side tile table and XCD-aware
+//    tile order as grouped_gemm_kernel; SwiGLU pairs the w1 and w3 rows of
+//    the same output columns inside each wave.
+#include <math.h>
+
+#include "gemm_common.h"
+
+namespace moe {
+namespace {
+
+constexpr int BKE = 32;      // k elements per stage (64 bytes of bf16)
+constexpr int NSTAGE = 4;    // LDS ring depth (loads run NSTAGE-1 stages ahead)
+constexpr int kGM = 4;       // m-tiles per strip
+
+#define MOE_GPTR(p) ((const void __attribute__((address_space(1)))*)(p))
+#define MOE_LPTR(p) ((void __attribute__((address_space(3)))*)(p))
+
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+// Waits until the global_load_lds of this wave for the current stage are
+// done (at most `ahead` later stages of LPW loads each still in flight) and
+// the LDS reads of the previous stage have returned, then synchronises the
+// workgroup.
+template <int LPW>
+__device__ __forceinline__ void wait_stage_and_barrier(int ahead) {
+  static_assert(2 * LPW <= 63, "vmcnt range");
+  if (ahead >= 2) {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * LPW) : "memory");
+  } else if (ahead == 1) {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LPW) : "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+}
+
+template <int NTHREADS>
+__device__ void scan_pairs_dma(int v0, int v1, int* out0, int* out1, int* total, int* sh) {
+  const int lane = lane_id();
+  const int w = threadIdx.x / 64;
+  const int s = v0 + v1;
+  int incl = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) sh[w] = incl;
+  __syncthreads();
+  int add = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NTHREADS / 64; ++i) {
+    if (i < w) add += sh[i];
+    tot += sh[i];
+  }
+  const int excl = incl - s + add;
+  *out0 = excl;
+  *out1 = excl + v0;
+  *total = tot;
+}
+
+template <int EPI, int BM, int BN, int WM_, int WN_>
+__global__ void __launch_bounds__(64 * WM_ * WN_, 1) dma_gemm_kernel(GroupedParams p) {
+  constexpr int NW = WM_ * WN_;                  // waves
+  constexpr int kThreads = 64 * NW;
+  constexpr int WTM = BM / WM_, WTN = BN / WN_;  // wave tile
+  constexpr int QM = WTM / 32, QN = WTN / 32;    // 32x32 subtiles per wave
+  constexpr int STAGE_BYTES = (BM + BN) * BKE * 2;
+  constexpr int A_BLOCKS = BM / 16, B_BLOCKS = BN / 16;   // 1 KB blocks per stage
+  constexpr int LPW = (A_BLOCKS + B_BLOCKS) / NW;         // DMA instructions per wave per stage
+  static_assert((A_BLOCKS + B_BLOCKS) % NW == 0, "blocks split evenly over waves");
+  static_assert(EPI != EPI_SWIGLU || QN % 2 == 0, "SwiGLU pairs subtiles");
+  static_assert(2 * kThreads >= kMaxGroups + 1, "tile table needs two entries per thread");
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* ring = smem;  // [NSTAGE][A 16 KB | B 16 KB]
+  int* s_tstart = reinterpret_cast<int*>(smem + NSTAGE * STAGE_BYTES);
+  int* s_rows = s_tstart + (kMaxGroups + 1);
+  int* s_r0 = s_rows + kMaxGroups;
+  int* s_scan = s_r0 + kMaxGroups;
+
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid / 64;
+  const int wm = wave / WN_, wn = wave % WN_;
+  const int ngroups = p.n_routed + (p.t_dense > 0 ? 1 : 0);
+  const int nt = p.N / BN;
+
+  {
+    int t2[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int g = 2 * tid + h;
+      int rows = 0, r0 = 0;
+      if (g < p.n_routed) {
+        r0 = p.off[p.e_begin + g];
+        rows = p.off[p.e_begin + g + 1] - r0;
+      } else if (g < ngroups) {
+        rows = (int)p.t_dense;
+      }
+      if (g < kMaxGroups) {
+        s_rows[g] = rows;
+        s_r0[g] = r0;
+      }
+      t2[h] = (g < ngroups) ? ((rows + BM - 1) / BM) * nt : 0;
+    }
+    int e0, e1, tot;
+    scan_pairs_dma<kThreads>(t2[0], t2[1], &e0, &e1, &tot, s_scan);
+    if (2 * tid < kMaxGroups + 1) s_tstart[2 * tid] = e0;
+    if (2 * tid + 1 < kMaxGroups + 1) s_tstart[2 * tid + 1] = e1;
+    if (tid == 0) s_tstart[ngroups] = tot;
+  }
+  __syncthreads();
+  const int total = s_tstart[ngroups];
+  const int G = gridDim.x;
+  const int first = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
+  const int a_sub = (p.a_shift && p.n_routed > 0) ? p.off[p.e_begin] : 0;
+  const int c_sub = (p.c_shift && p.n_routed > 0) ? p.off[p.e_begin] : 0;
+  const int64_t stride = (int64_t)p.K * 2;  // bytes per row of A and B
+  const int KT = p.K / BKE;
+
+  // DMA lane mapping inside a 1 KB block: position l -> row l/4, physical
+  // chunk l%4, logical chunk (l%4) ^ swz(l/4).
+  const int dr = lane >> 2;
+  const int dchunk = (lane & 3) ^ swz(dr);
+
+  for (int tile = first; tile < total; tile += G) {
+    int lo = 0, hi = ngroups - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_tstart[mid] <= tile) lo = mid; else hi = mid - 1;
+    }
+    const int g = lo;
+    const int local = tile - s_tstart[g];
+    const int rows = s_rows[g];
+    const int mt = (rows + BM - 1) / BM;
+    const int strip = local / (kGM * nt);
+    const int rem = local - strip * kGM * nt;
+    const int gm = min(kGM, mt - strip * kGM);
+    const int m_t = strip * kGM + rem % gm;
+    const int n_t = rem / gm;
+    const bool dense = g >= p.n_routed;
+    const int m0 = m_t * BM;
+
+    const unsigned char *A, *B1, *B3;
+    bf16_t* C;
+    if (!dense) {
+      A = reinterpret_cast<const unsigned char*>(p.a_routed) + (int64_t)(s_r0[g] - a_sub) * stride;
+      C = reinterpret_cast<bf16_t*>(p.c_routed) + (int64_t)(s_r0[g] - c_sub) * p.ldc;
+      B1 = reinterpret_cast<const unsigned char*>(p.b1) + (int64_t)g * p.b_stride * 2;
+      B3 = p.b3 ? reinterpret_cast<const unsigned char*>(p.b3) + (int64_t)g * p.b_stride * 2 : B1;
+    } else {
+      A = reinterpret_cast<const unsigned char*>(p.a_dense);
+      C = reinterpret_cast<bf16_t*>(p.c_dense);
+      B1 = reinterpret_cast<const unsigned char*>(p.bd1);
+      B3 = p.bd3 ? reinterpret_cast<const unsigned char*>(p.bd3) : B1;
+    }
+
+    // DMA instruction i of this wave fills 1 KB block b = wave + NW*i of the
+    // stage (A blocks first, then B blocks); lane -> tile row 16*(b mod
+    // blocks) + dr.  SwiGLU: each half of a wave column's B rows is w1 or w3
+    // of the same output columns.
+    const unsigned char* src[LPW];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int b = wave + NW * i;
+      if (b < A_BLOCKS) {
+        const int ar = min(m0 + 16 * b + dr, rows - 1);
+        src[i] = A + (int64_t)ar * stride + dchunk * 16;
+      } else {
+        const int tr = 16 * (b - A_BLOCKS) + dr;  // B tile row
+        int brow;
+        const unsigned char* bm = B1;
+        if (EPI == EPI_SWIGLU) {
+          const int col_wave = tr / WTN, rr = tr % WTN;
+          bm = (rr >= WTN / 2) ? B3 : B1;
+          brow = n_t * (BN / 2) + col_wave * (WTN / 2) + rr % (WTN / 2);
+        } else {
+          brow = n_t * BN + tr;
+        }
+        src[i] = bm + (int64_t)brow * stride + dchunk * 16;
+      }
+    }
+    auto issue = [&](int kt) {
+      unsigned char* st = ring + (kt % NSTAGE) * STAGE_BYTES;
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int b = wave + NW * i;
+        __builtin_amdgcn_global_load_lds(MOE_GPTR(src[i] + (int64_t)kt * (BKE * 2)),
+                                         MOE_LPTR(st + b * 1024), 16, 0, 0);
+      }
+    };
+
+    f32x16 acc[QM][QN];
+#pragma unroll
+    for (int i = 0; i < QM; ++i)
+#pragma unroll
+      for (int j = 0; j < QN; ++j) acc[i][j] = f32x16{};
+
+    // every wave has finished reading the ring of the previous tile
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int s = 0; s < NSTAGE - 1; ++s)
+      if (s < KT) issue(s);
+
+    for (int kt = 0; kt < KT; ++kt) {
+      wait_stage_and_barrier<LPW>(min(NSTAGE - 2, KT - 1 - kt));
+      if (kt + NSTAGE - 1 < KT) issue(kt + NSTAGE - 1);
+      const unsigned char* st = ring + (kt % NSTAGE) * STAGE_BYTES;
+#pragma unroll
+      for (int step = 0; step < BKE / 16; ++step) {
+        const int c = step * 2 + (lane >> 5);  // logical 16-byte chunk of this lane
+        u32x4 bfr[QN];
+#pragma unroll
+        for (int j = 0; j < QN; ++j) {
+          const int R = wn * WTN + j * 32 + (lane & 31);  // B tile row
+          const int r = R & 15;
+          bfr[j] = *reinterpret_cast<const u32x4*>(st + (A_BLOCKS + R / 16) * 1024 +
+                                                   (r * 4 + (c ^ swz(r))) * 16);
+        }
+#pragma unroll
+        for (int i = 0; i < QM; ++i) {
+          const int R = wm * WTM + i * 32 + (lane & 31);  // A tile row
+          const int r = R & 15;
+          const u32x4 af =
+              *reinterpret_cast<const u32x4*>(st + (R / 16) * 1024 + (r * 4 + (c ^ swz(r))) * 16);
+#pragma unroll
+          for (int j = 0; j < QN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8_t, af), __builtin_bit_cast(bf16x8_t, bfr[j]), acc[i][j],
+                0, 0, 0);
+        }
+      }
+    }
+
+    // epilogue: value v of a lane is row 8*(v/4) + 4*(lane/32) + v%4,
+    // column lane%32 of its 32x32 subtile
+#pragma unroll
+    for (int i = 0; i < QM; ++i) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = m0 + wm * WTM + i * 32 + 8 * (v / 4) + 4 * (lane >> 5) + (v % 4);
+        if (row >= rows) continue;
+        bf16_t* crow = C + (int64_t)row * p.ldc;
+        if (EPI == EPI_SWIGLU) {
+#pragma unroll
+          for (int j = 0; j < QN / 2; ++j) {
+            const int col = n_t * (BN / 2) + wn * (WTN / 2) + j * 32 + (lane & 31);
+            crow[col] = (bf16_t)f32_to_bf16(act_silu(acc[i][j][v]) * acc[i][j + QN / 2][v]);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < QN; ++j) {
+            const int col = n_t * BN + wn * WTN + j * 32 + (lane & 31);
+            float x = acc[i][j][v];
+            if (EPI == EPI_RELU) x = fmaxf(x, 0.f);
+            if (EPI == EPI_GELU) x = act_gelu(x);
+            crow[col] = (bf16_t)f32_to_bf16(x);
+          }
+        }
+      }
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+template <int EPI, int BM, int BN, int WM_, int WN_>
+moe_status launch_dma(const GroupedParams& p, int64_t max_routed_rows, hipStream_t stream) {
+  auto kern = dma_gemm_kernel<EPI, BM, BN, WM_, WN_>;
+  constexpr size_t lds = NSTAGE * (BM + BN) * BKE * 2 + (3 * kMaxGroups + 1 + 4) * sizeof(int);
+  static bool attr_set = false;
+  if (!attr_set) {
+    MOE_CHECK_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                      (int)lds));
+    attr_set = true;
+  }
+  const int nt = p.N / BN;
+  const int ngroups = p.n_routed + (p.t_dense > 0 ? 1 : 0);
+  const int64_t m_tiles_ub = (max_routed_rows + BM - 1) / BM + p.n_routed +
+                             (p.t_dense > 0 ? (p.t_dense + BM - 1) / BM : 0);
+  const int64_t tiles_ub = m_tiles_ub * nt;
+  if (ngroups == 0 || tiles_ub == 0) return MOE_OK;
+  int64_t grid = device_info().cus;
+  if (grid > tiles_ub) grid = tiles_ub;
+  if (grid >= 8) grid = grid / 8 * 8;
+  kern<<<(int)grid, 64 * WM_ * WN_, lds, stream>>>(p);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
+// Tile shapes: 256x256 with 2x4 waves of 128x64 for large groups; 128-row
+// tiles for groups of a few hundred rows (less padding).
+#ifndef MOE_DMA_BIG_WN
+#define MOE_DMA_BIG_WN 4
+#endif
+template <int EPI>
+moe_status launch_dma_shape(const GroupedParams& p, int64_t max_routed_rows, hipStream_t s) {
+  const int groups = p.n_routed > 0 ? p.n_routed : 1;
+  const bool small_groups = p.t_dense == 0 && max_routed_rows / groups < 768;
+  if (small_groups) return launch_dma<EPI, 128, 256, 1, 4>(p, max_routed_rows, s);
+  return launch_dma<EPI, 256, 256, 2, MOE_DMA_BIG_WN>(p, max_routed_rows, s);
+}
+
+}  // namespace
+
+bool dma_gemm_supported(const GroupedParams& p, bool bf16_weights) {
+  return bf16_weights && p.N % 256 == 0 && p.K % BKE == 0;
+}
+
+moe_status launch_dma_gemm(int epi, const GroupedParams& p, int64_t max_routed_rows,
+                           hipStream_t stream) {
+  switch (epi) {
+    case EPI_RELU:
+      return launch_dma_shape<EPI_RELU>(p, max_routed_rows, stream);
+    case EPI_GELU:
+      return launch_dma_shape<EPI_GELU>(p, max_routed_rows, stream);
+    case EPI_SWIGLU:
+      return launch_dma_shape<EPI_SWIGLU>(p, max_routed_rows, stream);
+    default:
+      return launch_dma_shape<EPI_NONE>(p, max_routed_rows, stream);
+  }
+}
+
+}  // namespace moe

@@ -36,6 +36,16 @@
 #include "gemm.h"
 #include "gemm_common.h"
 
+// Many-row bf16 groups use the LDS-DMA 256x256 kernel when shapes allow.
+#ifndef MOE_USE_DMA_GEMM
+#define MOE_USE_DMA_GEMM 1
+#endif
+
+// Padding (bytes) after each LDS tile row of the LDS-staged kernel.
+#ifndef MOE_LDS_PAD
+#define MOE_LDS_PAD 16
+#endif
+
 namespace moe {
 namespace {
 
@@ -73,7 +83,7 @@ __global__ void __launch_bounds__(kThreads, MINB) grouped_gemm_kernel(GroupedPar
   // RB: bytes of a tile row per K-stage (128 or 64); LDS rows are padded by
   // 16 bytes so the 16 lanes reading one MFMA fragment hit distinct banks.
   constexpr int kRowBytes = RB;
-  constexpr int kLdsRow = RB + 16;
+  constexpr int kLdsRow = RB + MOE_LDS_PAD;
   constexpr int CPR = RB / 16;               // 16-byte chunks per row
   constexpr int RPP = kThreads / CPR;        // rows covered by one pass of the block
   constexpr int STEPS = RB / 64;             // MFMA k-steps per stage
@@ -394,7 +404,7 @@ __global__ void __launch_bounds__(kThreads, MINB) grouped_gemm_kernel(GroupedPar
 
 template <int BM, int BN, int RB>
 constexpr size_t lds_bytes() {
-  return 2 * (BM + BN) * (RB + 16) + (3 * kMaxGroups + 1 + 4) * sizeof(int);
+  return 2 * (BM + BN) * (RB + MOE_LDS_PAD) + (3 * kMaxGroups + 1 + 4) * sizeof(int);
 }
 
 struct LaunchCfg {
@@ -554,6 +564,14 @@ moe_status run_ffn(const moe_ffn_args* a, const FfnPlan& pl, void* ws, hipStream
     if (st != MOE_OK) return st;
     if (mid_event) MOE_CHECK_HIP(hipEventRecord(mid_event, stream));
     st = launch<AT, AT, BSRC, EPI_NONE, 128, 128, 2, 2, 2>(p2, rows, stream);
+  } else if (MOE_USE_DMA_GEMM && dma_gemm_supported(p1, BSRC == B_SAME) &&
+             dma_gemm_supported(p2, BSRC == B_SAME)) {
+    p1.ksplit = p2.ksplit = 1;
+    const int epi1 = a->act == MOE_RELU ? EPI_RELU : (a->act == MOE_GELU ? EPI_GELU : EPI_SWIGLU);
+    st = launch_dma_gemm(epi1, p1, rows, stream);
+    if (st != MOE_OK) return st;
+    if (mid_event) MOE_CHECK_HIP(hipEventRecord(mid_event, stream));
+    st = launch_dma_gemm(EPI_NONE, p2, rows, stream);
   } else {
     p1.ksplit = p2.ksplit = 1;
     st = launch_gemm1<AT, BSRC, MOE_BIG_BM, MOE_BIG_BN, 2, 2, MOE_BIG_MINB>(a->act, p1, rows, stream);
