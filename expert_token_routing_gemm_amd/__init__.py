@@ -99,6 +99,14 @@ def moe_combine(a: CombineArgs, stream=None) -> None:
     _check(lib().moe_combine(C.byref(a), _stream(stream)), "moe_combine")
 
 
+def moe_bias_update(counts: torch.Tensor, b_select: torch.Tensor, T: int, k: int, gamma: float,
+                    stream=None) -> None:
+    """In-place bias-balancing step on device tensors counts [E] (int32) and
+    b_select [E] (float32)."""
+    _check(lib().moe_bias_update(_p(counts), _p(b_select), int(counts.numel()), int(T), int(k),
+                                 float(gamma), _stream(stream)), "moe_bias_update")
+
+
 def moe_layer_forward(a: LayerArgs, workspace: Optional[torch.Tensor], stream=None) -> None:
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().moe_layer_forward(C.byref(a), _p(workspace), ws_bytes, _stream(stream)),
@@ -138,11 +146,13 @@ class MoELayer:
     to the identical-logits mode."""
 
     def __init__(self, wl, device="cuda", capacity: Optional[int] = None,
-                 logits_input: Optional[np.ndarray] = None, keep_logits: bool = True):
+                 logits_input: Optional[np.ndarray] = None, keep_logits: bool = True,
+                 n_groups: int = 0, topk_groups: int = 0):
         self.wl = wl
         dev = torch.device(device)
         self.device = dev
         T, d, E, k, R, h = wl.T, wl.d, wl.E, wl.k, wl.R, wl.h
+        self.T, self.k = T, k
         self.act_dtype = DTYPE[wl.act_dtype]
         tdt = torch.float32 if wl.act_dtype == "f32" else torch.bfloat16
         self.capacity = moe_capacity(T, k, E, wl.cf) if capacity is None else int(capacity)
@@ -189,6 +199,7 @@ class MoELayer:
         r = a.route
         r.T, r.d, r.E, r.k = T, d, E, k
         r.act_dtype, r.score, r.renorm = self.act_dtype, SCORE[wl.score], int(bool(wl.renorm))
+        r.n_groups, r.topk_groups = int(n_groups), int(topk_groups)
         r.x = None if self.identical_logits else _p(self.x)
         r.w_router = _p(self.w_router)
         r.b_router = None if self.identical_logits else _p(self.b_router)
@@ -224,6 +235,12 @@ class MoELayer:
         self.workspace = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
 
     # single stages (each one C call)
+    def update_bias(self, gamma: float, stream=None) -> None:
+        """One bias-balancing step from the last dispatch's raw counts."""
+        if self.b_select is None:
+            raise ValueError("the workload has no selection bias")
+        moe_bias_update(self.counts, self.b_select, self.T, self.k, gamma, stream)
+
     def route(self, stream=None):
         moe_route(self.args.route, self.workspace, stream)
 

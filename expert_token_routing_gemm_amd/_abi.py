@@ -27,6 +27,7 @@ vp = C.c_void_p
 class RouteArgs(C.Structure):
     _fields_ = [("T", C.c_int64), ("d", C.c_int32), ("E", C.c_int32), ("k", C.c_int32),
                 ("act_dtype", C.c_int32), ("score", C.c_int32), ("renorm", C.c_int32),
+                ("n_groups", C.c_int32), ("topk_groups", C.c_int32),
                 ("x", vp), ("w_router", vp), ("b_router", vp), ("b_select", vp),
                 ("logits", vp), ("ids", vp), ("weights", vp)]
 
@@ -66,6 +67,7 @@ PROTOTYPES = {
     "moe_route": (C.c_int, [C.POINTER(RouteArgs), vp, C.c_size_t, vp]),
     "moe_capacity": (C.c_int32, [C.c_int64, C.c_int32, C.c_int32, C.c_double]),
     "moe_send_rows_max": (C.c_int64, [C.c_int64, C.c_int32, C.c_int32, C.c_int32]),
+    "moe_bias_update": (C.c_int, [vp, vp, C.c_int32, C.c_int64, C.c_int32, C.c_float, vp]),
     "moe_dispatch_workspace_bytes": (C.c_size_t, [C.POINTER(DispatchArgs)]),
     "moe_dispatch": (C.c_int, [C.POINTER(DispatchArgs), vp, C.c_size_t, vp]),
     "moe_ffn_workspace_bytes": (C.c_size_t, [C.POINTER(FfnArgs)]),

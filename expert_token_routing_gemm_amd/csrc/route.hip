@@ -353,10 +353,70 @@ __global__ void __launch_bounds__(256) logits_valu_kernel(const T* __restrict__ 
 // One wave per token.  Lane l owns experts l, l+64, l+128, l+192.
 // `add_bias` adds b_router to the logits read (raw GEMM output) and, if
 // logits_out is set, writes the final logits back.
+// Group-limited selection (ng > 0, tg < ng): group scores are the largest
+// key per group, gathered into lane g; tg rounds of wave arg-max pick the
+// groups; keys outside them become -inf.
+__device__ __forceinline__ void group_limit(float (&key)[MOE_MAX_EXPERTS / kWave], int E, int ng,
+                                            int tg) {
+  constexpr int PER = MOE_MAX_EXPERTS / kWave;
+  const int lane = lane_id();
+  const int gs = E / ng;
+  float gmax = -INFINITY;  // lane g < ng: score of group g
+  if (gs < kWave) {
+    // groups are aligned runs of gs lanes inside a slot: segmented max
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      float v = key[i];
+      for (int o = 1; o < gs; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+      const int gbase = (kWave * i) / gs;           // first group of slot i
+      const int src = (lane - gbase) * gs;           // leader lane of group `lane`
+      const bool mine = lane >= gbase && lane < gbase + kWave / gs && kWave * i < E;
+      const float got = __shfl(v, mine ? src : 0, kWave);
+      if (mine) gmax = got;
+    }
+  } else {
+    // a group spans gs / 64 whole slots
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      float v = key[i];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+      if (kWave * i < E && lane == (kWave * i) / gs) gmax = fmaxf(gmax, v);
+    }
+  }
+  // pick tg groups: (score desc, group asc)
+  bool taken = lane >= ng;
+  bool chosen = false;
+  for (int r = 0; r < tg; ++r) {
+    float bk = taken ? -INFINITY : gmax;
+    int bi = taken ? 0x7fffffff : lane;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ok = __shfl_xor(bk, o, kWave);
+      const int oi = __shfl_xor(bi, o, kWave);
+      if (key_better(ok, oi, bk, bi)) {
+        bk = ok;
+        bi = oi;
+      }
+    }
+    if (lane == bi) {
+      taken = true;
+      chosen = true;
+    }
+  }
+  const uint64_t sel = ballot(chosen);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane + kWave * i;
+    if (e < E && !((sel >> (e / gs)) & 1ull)) key[i] = -INFINITY;
+  }
+}
+
 __global__ void __launch_bounds__(256) topk_kernel(
     const float* __restrict__ logits_in, const float* __restrict__ b_router,
     const float* __restrict__ b_select, float* __restrict__ logits_out, int32_t* __restrict__ ids,
-    float* __restrict__ weights, int64_t T_tok, int E, int k, int score, int renorm) {
+    float* __restrict__ weights, int64_t T_tok, int E, int k, int score, int renorm, int ng,
+    int tg) {
   constexpr int PER = MOE_MAX_EXPERTS / kWave;  // 4
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
@@ -383,6 +443,7 @@ __global__ void __launch_bounds__(256) topk_kernel(
         }
       }
     }
+    if (ng > 0 && tg < ng) group_limit(key, E, ng, tg);
     int sel_e = -1;      // lane j < k keeps the j-th selection
     float sel_v = 0.f;   // its logit (softmax) or sigmoid score
     float first_logit = 0.f;
@@ -453,9 +514,21 @@ int grid_for(int64_t units, int per_block) {
   return (int)(want < 1 ? 1 : (want > cap ? cap : want));
 }
 
+bool grouped(const moe_route_args* a) { return a->n_groups > 0 && a->topk_groups < a->n_groups; }
+
 bool small_route_fits(const moe_route_args* a) {
   const size_t es = a->act_dtype == MOE_F32 ? 4 : 2;
-  return a->E <= 8 && (size_t)a->E * a->d * es <= 64 * 1024;
+  return !grouped(a) && a->E <= 8 && (size_t)a->E * a->d * es <= 64 * 1024;
+}
+
+__global__ void __launch_bounds__(256) bias_update_kernel(const int32_t* __restrict__ counts,
+                                                         float* __restrict__ b, int E, int64_t tk,
+                                                         float gamma) {
+  const int e = threadIdx.x;
+  if (e >= E) return;
+  const int64_t c = (int64_t)counts[e] * E;
+  const float s = c > tk ? 1.f : (c < tk ? -1.f : 0.f);
+  b[e] = b[e] - gamma * s;
 }
 
 bool mfma_route(const moe_route_args* a) {
@@ -484,6 +557,16 @@ extern "C" moe_status moe_route(const moe_route_args* a, void* ws, size_t ws_byt
                 "b_select needs sigmoid scores");
   MOE_CHECK_ARG(a->act_dtype == MOE_F32 || a->act_dtype == MOE_BF16, "bad act_dtype");
   MOE_CHECK_ARG(a->ids && a->weights, "ids/weights are required");
+  if (a->n_groups > 0) {
+    MOE_CHECK_ARG(a->n_groups <= 64 && a->E % a->n_groups == 0, "n_groups must divide E, <= 64");
+    const int gs = a->E / a->n_groups;
+    MOE_CHECK_ARG((gs < 64 && (gs & (gs - 1)) == 0) || gs % 64 == 0,
+                  "E/n_groups must be a power of two below 64 or a multiple of 64");
+    MOE_CHECK_ARG(a->topk_groups >= 0, "topk_groups < 0");
+    MOE_CHECK_ARG(!grouped(a) || (int64_t)a->k <= (int64_t)a->topk_groups * gs,
+                  "k exceeds the experts of topk_groups groups");
+    MOE_CHECK_ARG(!grouped(a) || a->topk_groups >= 1, "topk_groups must be >= 1");
+  }
   MOE_CHECK_ARG(aligned16(a->ids) && aligned16(a->weights), "ids/weights not 16-byte aligned");
   if (a->T == 0) return MOE_OK;
   const int tb = 256;
@@ -492,7 +575,8 @@ extern "C" moe_status moe_route(const moe_route_args* a, void* ws, size_t ws_byt
     MOE_CHECK_ARG(a->b_router == nullptr, "x == NULL: logits are final, b_router must be NULL");
     topk_kernel<<<grid_for(a->T, 4), tb, 0, stream>>>(a->logits, nullptr, a->b_select, nullptr,
                                                        a->ids, a->weights, a->T, a->E, a->k,
-                                                       a->score, a->renorm);
+                                                       a->score, a->renorm,
+                                                       grouped(a) ? a->n_groups : 0, a->topk_groups);
     MOE_CHECK_LAUNCH();
     return MOE_OK;
   }
@@ -557,7 +641,19 @@ extern "C" moe_status moe_route(const moe_route_args* a, void* ws, size_t ws_byt
   }
   topk_kernel<<<grid_for(a->T, 4), tb, 0, stream>>>(raw, a->b_router, a->b_select, a->logits,
                                                      a->ids, a->weights, a->T, a->E, a->k,
-                                                     a->score, a->renorm);
+                                                     a->score, a->renorm,
+                                                     grouped(a) ? a->n_groups : 0, a->topk_groups);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_bias_update(const int32_t* counts, float* b_select, int32_t E, int64_t T,
+                                      int32_t k, float gamma, hipStream_t stream) {
+  clear_error();
+  MOE_CHECK_ARG(E >= 1 && E <= MOE_MAX_EXPERTS, "E out of range [1, 256]");
+  MOE_CHECK_ARG(T >= 0 && k >= 1, "bad T or k");
+  MOE_CHECK_ARG(counts && b_select, "null pointer");
+  bias_update_kernel<<<1, 256, 0, stream>>>(counts, b_select, E, T * (int64_t)k, gamma);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }

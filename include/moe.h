@@ -73,6 +73,13 @@ typedef enum { MOE_RELU = 0, MOE_GELU = 1, MOE_SWIGLU = 2 } moe_act;
  *                   p[ids[t, j]]                         (renorm = 0).
  * Identical-logits mode: x == NULL.  Then `logits` is an INPUT holding the
  * final fp32 logits (b_router must be NULL) and only scores and top-k run.
+ * Group-limited selection (n_groups > 0, 0 < topk_groups < n_groups): the E
+ * experts form n_groups contiguous equal groups (nodes); a token may only use
+ * experts of its topk_groups best groups, a group's score being its largest
+ * selection key (ties: lower group index); the other experts' keys count as
+ * -infinity (DeepSeek-V3 limits each token to experts on 4 nodes: Ultralytics,
+ * "Load Balancing and Capacity").  Requires n_groups <= 64, E % n_groups == 0,
+ * E/n_groups a power of two or a multiple of 64, and k <= topk_groups*E/n_groups.
  */
 typedef struct moe_route_args {
   int64_t T;              /* tokens */
@@ -80,6 +87,8 @@ typedef struct moe_route_args {
   int32_t act_dtype;      /* MOE_F32 or MOE_BF16: dtype of x and w_router */
   int32_t score;          /* moe_score */
   int32_t renorm;         /* 1: renormalise the weights over the k selected */
+  int32_t n_groups;       /* expert groups for group-limited selection, 0 = off */
+  int32_t topk_groups;    /* groups a token may use (0 or >= n_groups = no limit) */
   const void* x;          /* [T, d] hidden states, or NULL (see above) */
   const void* w_router;   /* [E, d] */
   const float* b_router;  /* [E] added to the logits, or NULL */
@@ -141,6 +150,18 @@ int64_t moe_send_rows_max(int64_t T, int32_t k, int32_t E, int32_t capacity);
 size_t moe_dispatch_workspace_bytes(const moe_dispatch_args* a);
 moe_status moe_dispatch(const moe_dispatch_args* a, void* workspace, size_t ws_bytes,
                         hipStream_t stream);
+
+/* Bias-based balancing step (Ultralytics, "Load Balancing and Capacity",
+ * bias bullet: after each step the selection bias of overloaded experts goes
+ * down and of idle ones up).  With the raw per-expert counts of a dispatch
+ * over T tokens and k choices:
+ *   b_select[e] -= gamma * sign(counts[e] * E - T * k)
+ * (the comparison with the mean load T*k/E made exactly in integers, the
+ * update in fp32).  The pages give no step size; gamma is the caller's.
+ * counts [E] and b_select [E] are device pointers; b_select is updated in
+ * place.  E <= 256. */
+moe_status moe_bias_update(const int32_t* counts, float* b_select, int32_t E, int64_t T,
+                           int32_t k, float gamma, hipStream_t stream);
 
 /* ------------------------------------------------------------- expert FFN
  * Local expert compute (Ultralytics, "How Tokens Move Between GPUs", step 3;

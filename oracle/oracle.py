@@ -168,6 +168,34 @@ def topk_select(key: np.ndarray, k: int) -> np.ndarray:
     return order[:, :k].astype(np.int32)
 
 
+def group_limit_keys(key32: np.ndarray, n_groups: int, topk_groups: int) -> np.ndarray:
+    """Group-limited routing: each token may use experts of at most
+    ``topk_groups`` of the ``n_groups`` contiguous expert groups (DeepSeek-V3
+    sends each token to experts on at most 4 nodes: Ultralytics, "Load
+    Balancing and Capacity", communication paragraph).  How the groups are
+    chosen is not on the pages; reading taken: a group's score is its largest
+    selection key, the best ``topk_groups`` groups are kept (score desc, group
+    index asc) and the keys of all other experts become -inf."""
+    T, E = key32.shape
+    gs = E // n_groups
+    gmax = key32.reshape(T, n_groups, gs).max(axis=2)
+    chosen = np.argsort(-gmax, axis=1, kind="stable")[:, :topk_groups]
+    keep = np.zeros((T, n_groups), dtype=bool)
+    np.put_along_axis(keep, chosen, True, axis=1)
+    return np.where(np.repeat(keep, gs, axis=1), key32, np.float32(-np.inf)).astype(F32)
+
+
+def group_gap(score64: np.ndarray, n_groups: int, topk_groups: int) -> np.ndarray:
+    """fp64 gap between the topk_groups-th and next group score (inf if all
+    groups are kept)."""
+    T, E = score64.shape
+    if topk_groups >= n_groups:
+        return np.full(T, np.inf)
+    gmax = score64.reshape(T, n_groups, E // n_groups).max(axis=2)
+    srt = -np.sort(-gmax, axis=1)
+    return srt[:, topk_groups - 1] - srt[:, topk_groups]
+
+
 def route_weights(p: np.ndarray, ids: np.ndarray, renorm: bool) -> np.ndarray:
     """Combine weights from the (unbiased) router scores of the selected
     experts: renormalised over the k selected ones, or the raw score."""
@@ -190,10 +218,11 @@ def selection_gap(p: np.ndarray, score: str, b_select, k: int) -> np.ndarray:
 
 
 def route(x64, wr64, b_router, b_select, k: int, score: str, renorm: bool,
-          logits32=None, ids_override=None) -> dict:
+          logits32=None, ids_override=None, n_groups: int = 0, topk_groups: int = 0) -> dict:
     """Route step.  ``logits32`` (optional) replaces the logits by given fp32
     values (the identical-logits mode); ``ids_override`` replaces the
-    selection by given ids (weights still follow the oracle's own scores)."""
+    selection by given ids (weights still follow the oracle's own scores).
+    ``n_groups``/``topk_groups`` > 0 enable group-limited selection."""
     if logits32 is not None:
         L = np.asarray(logits32, F32).astype(F64)
     else:
@@ -201,10 +230,33 @@ def route(x64, wr64, b_router, b_select, k: int, score: str, renorm: bool,
     L32 = L.astype(F32)
     p = route_scores(L, score)
     key32 = selection_keys32(L32, score, b_select)
+    grouped = n_groups > 0 and 0 < topk_groups < n_groups
+    if grouped:
+        key32 = group_limit_keys(key32, n_groups, topk_groups)
     ids = topk_select(key32, k) if ids_override is None else np.asarray(ids_override, np.int32)
     w = route_weights(p, ids, renorm)
-    gap = selection_gap(p, score, b_select, k)
+    if grouped:
+        s64 = p if (score == "softmax" or b_select is None) else p + np.asarray(b_select, F64)[None, :]
+        ggap = group_gap(s64, n_groups, topk_groups)
+        masked = np.where(np.isfinite(key32), s64, -np.inf)
+        srt = -np.sort(-masked, axis=1)
+        egap = srt[:, k - 1] - srt[:, k] if k < masked.shape[1] else np.full(len(srt), np.inf)
+        gap = np.minimum(ggap, np.where(np.isfinite(egap), egap, np.inf))
+    else:
+        gap = selection_gap(p, score, b_select, k)
     return dict(logits=L, logits32=L32, scores=p, key32=key32, ids=ids, weights=w, gap=gap)
+
+
+def bias_update(b_select32: np.ndarray, counts: np.ndarray, T: int, k: int, gamma: float) -> np.ndarray:
+    """Bias-based balancing after a step (Ultralytics, "Load Balancing and
+    Capacity", bias bullet): the bias of an expert loaded above the mean
+    T*k/E goes down, below the mean up.  The pages give no step size; rule
+    taken: b <- b - gamma * sign(count - T*k/E), the comparison made exactly in
+    integers (count*E vs T*k), the update in fp32."""
+    counts = np.asarray(counts, np.int64)
+    E = counts.size
+    sgn = np.sign(counts * E - np.int64(T) * k).astype(F32)
+    return (np.asarray(b_select32, F32) - np.float32(gamma) * sgn).astype(F32)
 
 
 # --------------------------------------------------------------------------
@@ -370,14 +422,17 @@ def combine(x64, shared64, ys64, ids, slot, w, e_begin: int, e_end: int) -> np.n
 # --------------------------------------------------------------------------
 
 
-def layer(wl, cf=None, logits32=None, ids_override=None, with_ffn=True) -> dict:
+def layer(wl, cf=None, logits32=None, ids_override=None, with_ffn=True, n_groups=0,
+          topk_groups=0) -> dict:
     """route -> dispatch -> pack -> expert FFN (+ shared) -> combine on a
     workload ``wl`` (attribute access only).  ``cf`` overrides the workload's
-    capacity factor; ``logits32`` / ``ids_override`` as in :func:`route`."""
+    capacity factor; ``logits32`` / ``ids_override`` / the group limit as in
+    :func:`route`."""
     x64 = to_f64(wl.x, wl.act_dtype)
     wr64 = to_f64(wl.w_router, wl.act_dtype)
     r = route(x64, wr64, wl.b_router, wl.b_select, wl.k, wl.score, wl.renorm,
-              logits32=logits32, ids_override=ids_override)
+              logits32=logits32, ids_override=ids_override, n_groups=n_groups,
+              topk_groups=topk_groups)
     C = capacity(wl.T, wl.k, wl.E, wl.cf if cf is None else cf)
     dsp = dispatch(r["ids"], wl.E, wl.R, C)
     out = dict(route=r, dispatch=dsp, capacity=C)

@@ -442,3 +442,95 @@ def test_softmax_selection_on_fp32_logits_matches_fp64_order(c0_route):
     ok = r["gap"] > 1e-6
     np.testing.assert_array_equal(r["ids"][ok], ids64[ok])
     np.testing.assert_allclose(r["weights"].sum(1), 1.0, rtol=1e-15)
+
+
+# ---------------------------------------------------------------- group-limited routing
+
+
+def _brute_group_topk(key, n_groups, M, k):
+    """Enumerate every set of M groups; the chosen set contains the best
+    group score, then the next best, ... (score desc, index asc); the experts
+    are the k best keys inside the chosen groups."""
+    T, E = key.shape
+    gs = E // n_groups
+    out = np.zeros((T, k), np.int64)
+    for t in range(T):
+        gscore = [max(key[t, g * gs:(g + 1) * gs]) for g in range(n_groups)]
+        best = None
+        for S in itertools.combinations(range(n_groups), M):
+            rest = [g for g in range(n_groups) if g not in S]
+            if all((gscore[a] > gscore[b]) or (gscore[a] == gscore[b] and a < b) for a in S for b in rest):
+                best = S
+                break
+        allowed = [e for e in range(E) if e // gs in best]
+        order = sorted(allowed, key=lambda e: (-float(key[t, e]), e))
+        out[t] = order[:k]
+    return out
+
+
+@settings(max_examples=40, deadline=None)
+@given(T=st.integers(1, 12), ng=st.sampled_from([2, 4, 8]), M=st.integers(1, 4), seed=st.integers(0, 9999),
+       ties=st.booleans())
+def test_group_limited_topk_bruteforce(T, ng, M, seed, ties):
+    E = 16
+    M = min(M, ng)
+    gs = E // ng
+    k = min(3, M * gs)
+    rng = np.random.default_rng(seed)
+    key = rng.standard_normal((T, E)).astype(np.float32)
+    if ties:
+        key = np.round(key * 2).astype(np.float32)
+    ids = O.topk_select(O.group_limit_keys(key, ng, M), k)
+    np.testing.assert_array_equal(ids, _brute_group_topk(key, ng, M, k))
+    # the chosen experts span at most M groups
+    assert all(len(set((ids[t] // gs).tolist())) <= M for t in range(T))
+
+
+def test_group_limit_reduces_to_plain_topk():
+    rng = np.random.default_rng(3)
+    key = rng.standard_normal((50, 256)).astype(np.float32)
+    np.testing.assert_array_equal(O.topk_select(O.group_limit_keys(key, 8, 8), 8), O.topk_select(key, 8))
+    one = O.topk_select(O.group_limit_keys(key, 8, 1), 8)
+    best_group = key.reshape(50, 8, 32).max(axis=2).argmax(axis=1)
+    np.testing.assert_array_equal(one // 32, np.repeat(best_group[:, None], 8, axis=1))
+
+
+def test_group_limited_route_weights_and_gap(c4_small):
+    wl = c4_small
+    x64 = O.to_f64(wl.x, "bf16")
+    wr64 = O.to_f64(wl.w_router, "bf16")
+    r = O.route(x64, wr64, None, wl.b_select, wl.k, "sigmoid", True, n_groups=8, topk_groups=4)
+    assert all(len(set((r["ids"][t] // 32).tolist())) <= 4 for t in range(wl.T))
+    np.testing.assert_allclose(r["weights"].sum(axis=1), 1.0, rtol=1e-14)
+    plain = O.route(x64, wr64, None, wl.b_select, wl.k, "sigmoid", True)
+    assert np.all(r["gap"] <= np.maximum(plain["gap"], r["gap"]))
+
+
+# ---------------------------------------------------------------- bias balancing
+
+
+def test_bias_update_rule_hand_example():
+    b = np.array([0.5, 0.0, -0.25], np.float32)
+    # T*k = 8 over E = 3: mean 8/3; loads 5 (over), 1 (under), 2 (under)
+    out = O.bias_update(b, [5, 1, 2], T=4, k=2, gamma=0.125)
+    np.testing.assert_array_equal(out, np.array([0.375, 0.125, -0.125], np.float32))
+    # an exactly average load keeps its bias (compared in integers, not floats)
+    np.testing.assert_array_equal(O.bias_update(b, [2, 2, 2], T=3, k=2, gamma=0.5), b)
+
+
+def test_bias_update_balances_skewed_routing():
+    """Iterating route -> histogram -> update on skewed synthetic logits
+    shrinks the busiest expert's load (the rule's purpose)."""
+    rng = np.random.default_rng(0)
+    T, E, k = 2048, 32, 4
+    L = (rng.standard_normal((T, E)) * 0.3 + np.linspace(1.0, -1.0, E)[None, :]).astype(np.float32)
+    b = np.zeros(E, np.float32)
+    first = None
+    for step in range(60):
+        ids = O.topk_select(O.selection_keys32(L, "sigmoid", b), k)
+        counts = np.bincount(ids.ravel(), minlength=E)
+        if first is None:
+            first = counts.max() / (T * k / E)
+        b = O.bias_update(b, counts, T, k, gamma=0.01)
+    last = counts.max() / (T * k / E)
+    assert first > 2.0 and last < 0.6 * first
