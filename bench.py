@@ -146,6 +146,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1, help="workload index 0-4 (default 1: decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--w-layout", choices=["rowmajor", "tiled"], default=None,
+                    help="expert weight layout (default: tiled for the decode workload, whose "
+                         "GEMMs stream weights; row-major otherwise)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead of the layer: time a plain device copy of MIB MiB (HBM "
                          "calibration for the traffic counters) and a full read (sum)")
@@ -168,7 +171,9 @@ def main():
         return
     print(f"[bench] generating workload {args.config}", file=sys.stderr, flush=True)
     wl = make_workload(args.config)
-    layer = M.MoELayer(wl, device="cuda:0", keep_logits=False)
+    w_layout = args.w_layout or ("tiled" if args.config == 1 else "rowmajor")
+    layer = M.MoELayer(wl, device="cuda:0", keep_logits=False,
+                       w_layout=M.MOE_W_TILED16 if w_layout == "tiled" else M.MOE_W_ROWMAJOR)
     hip = _hip()
     K, W = args.steps, args.warmup
     print(f"[bench] warmup {W}, timed {K}", file=sys.stderr, flush=True)
@@ -239,7 +244,8 @@ def main():
                                f"{wl.act} h={wl.h}, executed experts {wl.e_begin}-{wl.e_end - 1}"
                                f"{' + shared' if shared else ''}, capacity "
                                f"{'none' if wl.cf is None else wl.cf}",
-                   "tokens": wl.T, "parallelism": "one GPU's share (no collectives)"},
+                   "tokens": wl.T, "expert_weight_layout": w_layout,
+                   "parallelism": "one GPU's share (no collectives)"},
         "stages_ms": stage_ms,
         "stages_hbm_frac": stage_frac,
         "gemm_tflops": {k: flops[k] / (stage_ms[k] / 1e3) / 1e12 for k in flops},

@@ -20,7 +20,8 @@ import torch
 
 from . import _abi
 from ._abi import (INT32_MAX, MOE_BF16, MOE_F32, MOE_FP8_E4M3, MOE_GELU, MOE_LAYER_EVENTS,  # noqa: F401
-                   MOE_RELU, MOE_SIGMOID, MOE_SOFTMAX, MOE_SWIGLU, CombineArgs, DispatchArgs,
+                   MOE_RELU, MOE_SIGMOID, MOE_SOFTMAX, MOE_SWIGLU, MOE_W_ROWMAJOR, MOE_W_TILED16,
+                   CombineArgs, DispatchArgs,
                    FfnArgs, LayerArgs, RouteArgs, lib)
 
 DTYPE = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
@@ -107,6 +108,18 @@ def moe_bias_update(counts: torch.Tensor, b_select: torch.Tensor, T: int, k: int
                                  float(gamma), _stream(stream)), "moe_bias_update")
 
 
+def moe_weight_tile(w: torch.Tensor, n_mats: int, rows: int, stream=None) -> torch.Tensor:
+    """A new device tensor holding the n_mats [rows, *] matrices of ``w``
+    (contiguous) in the 16-row tiled layout of the streaming kernels."""
+    w = w.contiguous()
+    out = torch.empty_like(w)
+    nbytes = w.numel() * w.element_size()
+    row_bytes = nbytes // max(1, n_mats * rows)
+    _check(lib().moe_weight_tile(_p(w), _p(out), int(n_mats), int(rows), int(row_bytes),
+                                 _stream(stream)), "moe_weight_tile")
+    return out
+
+
 def moe_layer_forward(a: LayerArgs, workspace: Optional[torch.Tensor], stream=None) -> None:
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().moe_layer_forward(C.byref(a), _p(workspace), ws_bytes, _stream(stream)),
@@ -147,7 +160,7 @@ class MoELayer:
 
     def __init__(self, wl, device="cuda", capacity: Optional[int] = None,
                  logits_input: Optional[np.ndarray] = None, keep_logits: bool = True,
-                 n_groups: int = 0, topk_groups: int = 0):
+                 n_groups: int = 0, topk_groups: int = 0, w_layout: int = 0):
         self.wl = wl
         dev = torch.device(device)
         self.device = dev
@@ -173,6 +186,13 @@ class MoELayer:
         sh = wl.shared or {}
         self.ws1, self.ws3, self.ws2 = (to_device(sh.get("w1"), dev), to_device(sh.get("w3"), dev),
                                         to_device(sh.get("w2"), dev))
+        self.w_layout = int(w_layout)
+        if self.w_layout == _abi.MOE_W_TILED16:
+            nx = wl.e_end - wl.e_begin
+            til = lambda w, n, r: None if w is None else moe_weight_tile(w, n, r)  # noqa: E731
+            self.w1, self.w3, self.w2 = til(self.w1, nx, h), til(self.w3, nx, h), til(self.w2, nx, d)
+            self.ws1, self.ws3, self.ws2 = (til(self.ws1, 1, h), til(self.ws3, 1, h),
+                                            til(self.ws2, 1, d))
         self.ss1, self.ss3, self.ss2 = (to_device(sh.get("s1"), dev), to_device(sh.get("s3"), dev),
                                         to_device(sh.get("s2"), dev))
         # outputs
@@ -215,6 +235,7 @@ class MoELayer:
         f = a.ffn
         f.d, f.h, f.E, f.e_begin, f.e_end = d, h, E, wl.e_begin, wl.e_end
         f.act, f.act_dtype, f.w_dtype = ACT[wl.act], self.act_dtype, DTYPE[wl.w_dtype]
+        f.w_layout = self.w_layout
         f.max_rows = self.ffn_rows
         f.x_send, f.expert_off = _p(self.x_send), _p(self.expert_off)
         f.w1, f.w3, f.w2 = _p(self.w1), _p(self.w3), _p(self.w2)

@@ -16,6 +16,7 @@ MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_RELU, MOE_GELU, MOE_SWIGLU = 0, 1, 2
+MOE_W_ROWMAJOR, MOE_W_TILED16 = 0, 1
 MOE_MAX_EXPERTS = 256
 MOE_MAX_TOPK = 8
 MOE_LAYER_EVENTS = 6
@@ -43,7 +44,8 @@ class DispatchArgs(C.Structure):
 class FfnArgs(C.Structure):
     _fields_ = [("d", C.c_int32), ("h", C.c_int32), ("E", C.c_int32), ("e_begin", C.c_int32),
                 ("e_end", C.c_int32), ("act", C.c_int32), ("act_dtype", C.c_int32),
-                ("w_dtype", C.c_int32), ("max_rows", C.c_int64), ("x_send", vp),
+                ("w_dtype", C.c_int32), ("w_layout", C.c_int32), ("max_rows", C.c_int64),
+                ("x_send", vp),
                 ("expert_off", vp), ("w1", vp), ("w3", vp), ("w2", vp), ("s1", vp), ("s3", vp),
                 ("s2", vp), ("y_send", vp), ("T_dense", C.c_int64), ("x_dense", vp),
                 ("ws1", vp), ("ws3", vp), ("ws2", vp), ("ss1", vp), ("ss3", vp), ("ss2", vp),
@@ -72,6 +74,7 @@ PROTOTYPES = {
     "moe_dispatch": (C.c_int, [C.POINTER(DispatchArgs), vp, C.c_size_t, vp]),
     "moe_ffn_workspace_bytes": (C.c_size_t, [C.POINTER(FfnArgs)]),
     "moe_expert_ffn": (C.c_int, [C.POINTER(FfnArgs), vp, C.c_size_t, vp]),
+    "moe_weight_tile": (C.c_int, [vp, vp, C.c_int64, C.c_int32, C.c_int64, vp]),
     "moe_combine": (C.c_int, [C.POINTER(CombineArgs), vp]),
     "moe_workspace_bytes": (C.c_size_t, [C.POINTER(LayerArgs)]),
     "moe_layer_forward": (C.c_int, [C.POINTER(LayerArgs), vp, C.c_size_t, vp]),

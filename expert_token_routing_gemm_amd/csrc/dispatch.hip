@@ -14,8 +14,9 @@
 //   hist_kernel      : block b owns a chunk of TB tokens (TB*k <= 256
 //                      assignments); LDS-private histogram -> blk[b][e].
 //   scan_kernel      : one workgroup; per expert an exclusive scan over blocks
-//                      (in place in blk), counts, kept = min(counts, C), the
-//                      expert offsets by a wave-level scan, per-rank counts.
+//                      (in place in blk, split over up to 64 lanes), counts,
+//                      kept = min(counts, C), the expert offsets by a
+//                      wave-level scan, per-rank counts.
 //   rank_pack_kernel : recomputes each assignment's position: block base +
 //                      earlier waves of the block + lanes of its wave holding
 //                      the same expert (ballot / popcount), which is exactly
@@ -45,68 +46,94 @@ __global__ void __launch_bounds__(kThreads) hist_kernel(const int32_t* __restric
   for (int e = threadIdx.x; e < E; e += kThreads) blk[(int64_t)blockIdx.x * E + e] = cnt[e];
 }
 
-// Inclusive scan of one value per thread across a 256-thread block.
-__device__ int block_inclusive_scan(int v, int* sh_waves) {
-  const int lane = lane_id();
-  const int w = threadIdx.x / 64;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(v, off, 64);
-    if (lane >= off) v += o;
-  }
-  if (lane == 63) sh_waves[w] = v;
-  __syncthreads();
-  int add = 0;
-  for (int i = 0; i < w; ++i) add += sh_waves[i];
-  __syncthreads();
-  return v + add;
-}
+// scan_kernel: one workgroup of kScanThreads.  Expert e owns P consecutive
+// threads (P = largest power of two <= min(64, kScanThreads / E), so they are
+// lanes of one wave); thread p of expert e sums a contiguous chunk of the
+// per-block counts, a segmented wave scan turns the chunk sums into chunk
+// bases, and a second pass over the chunk writes each block's exclusive base
+// in place.  Loads of a chunk are independent, so the serial depth is the
+// chunk length (nblocks / P), not nblocks.
+constexpr int kScanThreads = 1024;
 
-__global__ void __launch_bounds__(kThreads) scan_kernel(
-    int32_t* __restrict__ blk, int nblocks, int E, int R, int C, int32_t* __restrict__ counts,
+__global__ void __launch_bounds__(kScanThreads) scan_kernel(
+    int32_t* __restrict__ blk, int nblocks, int E, int R, int C, int P, int32_t* __restrict__ counts,
     int32_t* __restrict__ kept, int32_t* __restrict__ off, int32_t* __restrict__ rank_counts,
     int32_t* __restrict__ rank_off) {
-  __shared__ int sh_waves[kWaves];
+  __shared__ int tot[MOE_MAX_EXPERTS];
+  __shared__ int wsum[MOE_MAX_EXPERTS / 64];
   __shared__ int sh_off[MOE_MAX_EXPERTS + 1];
-  const int e = threadIdx.x;
-  int total = 0;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int e = tid / P;
+  const int p = tid - e * P;
+  const int chunk = (nblocks + P - 1) / P;
+  const int b0 = min(p * chunk, nblocks);
+  const int b1 = min(b0 + chunk, nblocks);
+  int sum = 0;
   if (e < E) {
-    int b = 0;
-    for (; b + 4 <= nblocks; b += 4) {
-      int v[4];
+    int b = b0;
+    for (; b + 8 <= b1; b += 8) {
+      int v[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = blk[(int64_t)(b + i) * E + e];
+      for (int i = 0; i < 8; ++i) v[i] = blk[(int64_t)(b + i) * E + e];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        blk[(int64_t)(b + i) * E + e] = total;
-        total += v[i];
-      }
+      for (int i = 0; i < 8; ++i) sum += v[i];
     }
-    for (; b < nblocks; ++b) {
+    for (; b < b1; ++b) sum += blk[(int64_t)b * E + e];
+  }
+  // segmented inclusive scan over the P lanes of the expert
+  int incl = sum;
+  for (int o = 1; o < P; o <<= 1) {
+    const int u = __shfl_up(incl, o, 64);
+    if ((lane & (P - 1)) >= o) incl += u;
+  }
+  if (e < E) {
+    int run = incl - sum;
+    for (int b = b0; b < b1; ++b) {
       const int v = blk[(int64_t)b * E + e];
-      blk[(int64_t)b * E + e] = total;
-      total += v;
+      blk[(int64_t)b * E + e] = run;
+      run += v;
     }
+    if (p == P - 1) tot[e] = incl;
   }
-  const int kp = (e < E) ? min(total, C) : 0;
-  const int incl = block_inclusive_scan(kp, sh_waves);
-  if (e < E) {
-    counts[e] = total;
-    kept[e] = kp;
-    off[e] = incl - kp;
-    sh_off[e] = incl - kp;
+  __syncthreads();
+  // exclusive scan of kept over the experts (threads 0..255)
+  int kp = 0, ex = 0;
+  if (tid < MOE_MAX_EXPERTS) {
+    kp = tid < E ? min(tot[tid], C) : 0;
+    ex = kp;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(ex, o, 64);
+      if (lane >= o) ex += u;
+    }
+    if (lane == 63) wsum[tid / 64] = ex;
   }
-  if (e == E - 1) {
-    off[E] = incl;
-    sh_off[E] = incl;
+  __syncthreads();
+  if (tid < E) {
+    for (int i = 0; i < tid / 64; ++i) ex += wsum[i];
+    counts[tid] = tot[tid];
+    kept[tid] = kp;
+    off[tid] = ex - kp;
+    sh_off[tid] = ex - kp;
+    if (tid == E - 1) {
+      off[E] = ex;
+      sh_off[E] = ex;
+    }
   }
   __syncthreads();
   const int per = E / R;
-  for (int r = threadIdx.x; r < R; r += kThreads) {
+  for (int r = tid; r < R; r += kScanThreads) {
     rank_counts[r] = sh_off[(r + 1) * per] - sh_off[r * per];
     rank_off[r] = sh_off[r * per];
   }
-  if (threadIdx.x == 0) rank_off[R] = sh_off[E];
+  if (tid == 0) rank_off[R] = sh_off[E];
+}
+
+int scan_lanes(int E) {
+  int P = 64;
+  while (P > 1 && P * E > kScanThreads) P >>= 1;
+  return P;
 }
 
 template <int UNROLL>
@@ -419,9 +446,9 @@ extern "C" moe_status moe_dispatch(const moe_dispatch_args* a, void* ws, size_t 
                                                      p.tokens_per_block * a->k, a->E);
     MOE_CHECK_LAUNCH();
   }
-  scan_kernel<<<1, kThreads, 0, stream>>>(blk, a->T > 0 ? p.nblocks : 0, a->E, a->R, a->capacity,
-                                          a->counts, a->kept, a->expert_off, a->rank_counts,
-                                          a->rank_off);
+  scan_kernel<<<1, kScanThreads, 0, stream>>>(blk, a->T > 0 ? p.nblocks : 0, a->E, a->R,
+                                              a->capacity, scan_lanes(a->E), a->counts, a->kept,
+                                              a->expert_off, a->rank_counts, a->rank_off);
   MOE_CHECK_LAUNCH();
   if (a->T > 0) {
     rank_pack_kernel<4><<<p.nblocks, kThreads, 0, stream>>>(

@@ -524,6 +524,7 @@ moe_status run_ffn(const moe_ffn_args* a, const FfnPlan& pl, void* ws, hipStream
   p1.b_stride = (int64_t)h * d;
   p1.ks = d / 128;
   p1.ns = h / 128;
+  p1.b_tiled = a->w_layout == MOE_W_TILED16 ? 1 : 0;
   p1.partial = partial;
   p1.ksplit = pl.ks1;
   p1.max_rows = rows;
@@ -623,6 +624,7 @@ moe_status moe::expert_ffn_impl(const moe_ffn_args* a, void* ws, size_t ws_bytes
   MOE_CHECK_ARG(0 <= a->e_begin && a->e_begin <= a->e_end && a->e_end <= a->E,
                 "need 0 <= e_begin <= e_end <= E");
   MOE_CHECK_ARG(a->act == MOE_RELU || a->act == MOE_GELU || a->act == MOE_SWIGLU, "bad act");
+  MOE_CHECK_ARG(a->w_layout == MOE_W_ROWMAJOR || a->w_layout == MOE_W_TILED16, "bad w_layout");
   MOE_CHECK_ARG(a->max_rows >= 0 && a->T_dense >= 0, "negative row count");
   MOE_CHECK_ARG(a->max_rows + a->T_dense < (int64_t)1 << 31, "row count must fit in int32");
   const bool f32 = a->act_dtype == MOE_F32;
@@ -662,6 +664,11 @@ moe_status moe::expert_ffn_impl(const moe_ffn_args* a, void* ws, size_t ws_bytes
     return MOE_OK;
   }
   const FfnPlan pl = plan_ffn(a);
+  if (a->w_layout == MOE_W_TILED16 && !pl.small_m) {
+    set_error("moe_expert_ffn: tiled weights need the streaming path (bf16 activations, <= 64 "
+              "rows per executed expert, T_dense <= 64)");
+    return MOE_ERR_UNSUPPORTED;
+  }
   if (f32) return run_ffn<float, B_SAME>(a, pl, ws, stream, mid_event);
   if (fp8) return run_ffn<bf16_t, B_FP8>(a, pl, ws, stream, mid_event);
   return run_ffn<bf16_t, B_SAME>(a, pl, ws, stream, mid_event);

@@ -40,6 +40,7 @@ struct GroupedParams {
   int N;        // B rows covered by the tile grid (SwiGLU: 2 x output columns)
   int ldc;      // output columns
   int64_t b_stride;  // elements between two experts' weight matrices
+  int b_tiled;  // 1: weights in the 16-row tiled layout (moe_weight_tile)
   int ks;       // K / 128
   int ns;       // output-dim / 128 (scale rows)
   // split-K (weight-streaming kernel only): ksplit > 1 writes fp32 partial

@@ -43,8 +43,31 @@ constexpr int kThreads = kGemmThreads;
 #ifndef MOE_DN_SKIP
 #define MOE_DN_SKIP 0
 #endif
+// Weights are read exactly once per launch: nontemporal loads keep them from
+// displacing the activations in the caches and stream faster from HBM.
+#ifndef MOE_SG_NT
+#define MOE_SG_NT 1
+#endif
+// Lane-group K layout inside a chunk.  0: group q owns one contiguous run of
+// CK/4 elements.  1: interleaved, each 16-byte load of the wave covers 64
+// contiguous bytes of each of its 16 weight rows.
+#ifndef MOE_SG_IL
+#define MOE_SG_IL 1
+#endif
+// 1: A rows of a chunk are fetched one chunk ahead, before its weights.
+#ifndef MOE_SG_AHEAD
+#define MOE_SG_AHEAD 0
+#endif
 
-template <int BSRC, int EPI, int CK, int MINW>
+__device__ __forceinline__ u32x4 load_stream(const unsigned char* ptr) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(ptr);
+  if constexpr (MOE_SG_NT) return __builtin_nontemporal_load(p);
+  return *p;
+}
+
+// TL: weights in the 16-row tiled layout (each wave's loads of a chunk are
+// whole contiguous 1 KB pieces; see moe_weight_tile) instead of row-major.
+template <int BSRC, int EPI, int CK, int MINW, bool TL>
 __global__ void __launch_bounds__(kThreads, MINW) stream_gemm_kernel(GroupedParams p) {
   constexpr int NMAT = (EPI == EPI_SWIGLU) ? 2 : 1;
   constexpr int V = CK / 32;                 // 16-byte bf16 pieces per lane per matrix
@@ -53,7 +76,9 @@ __global__ void __launch_bounds__(kThreads, MINW) stream_gemm_kernel(GroupedPara
   constexpr int A_PIECES = MROWS * CK * 2 / 16 / kThreads;  // 16-byte A pieces per thread
   constexpr int QB = CK / 4;                 // K elements per lane group per chunk
   constexpr bool SKIP = (EPI == EPI_SWIGLU) ? MOE_SG_SKIP : MOE_DN_SKIP;
+  constexpr bool IL = MOE_SG_IL || TL;
   static_assert(A_PIECES >= 1, "chunk too small");
+  static_assert(BSRC != B_FP8 || CK <= 128, "one fp8 scale block per chunk");
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* lds_a = smem;  // [2][MROWS][RS]
 
@@ -100,7 +125,18 @@ __global__ void __launch_bounds__(kThreads, MINW) stream_gemm_kernel(GroupedPara
   // per-lane byte pointers into the weight rows (lane group q owns QB elements)
   const unsigned char* bptr[NMAT];
 #pragma unroll
-  for (int m = 0; m < NMAT; ++m) bptr[m] = Bm[m] + ((int64_t)brow * p.K + q * QB) * bes;
+  for (int m = 0; m < NMAT; ++m)
+    bptr[m] = TL ? Bm[m] + (int64_t)ocol0 * p.K * bes + lane * 16
+                 : Bm[m] + (int64_t)brow * p.K * bes + (IL ? q * 16 : q * QB * bes);
+  constexpr int VSTEP = TL ? 1024 : (IL ? 64 : 16);  // bytes between a lane's loads in a chunk
+  const int64_t cstride = TL ? (int64_t)CK * bes * 16 : (int64_t)CK * bes;  // per chunk
+  // K offset (elements, inside the chunk) of the 8 values lane group q feeds
+  // to MFMA step s; the A fragments use the same map
+  auto koff = [&](int s_) {
+    if constexpr (!IL) return q * QB + s_ * 8;
+    if constexpr (BSRC == B_FP8) return (s_ >> 1) * 64 + q * 16 + (s_ & 1) * 8;
+    return s_ * 32 + q * 8;
+  };
 
   u32x4 breg[2][NMAT][V];
   float bscale[2][NMAT];
@@ -109,14 +145,14 @@ __global__ void __launch_bounds__(kThreads, MINW) stream_gemm_kernel(GroupedPara
   {                                                                                        \
     _Pragma("unroll") for (int m = 0; m < NMAT; ++m) {                                     \
       if constexpr (BSRC == B_FP8) {                                                       \
-        const unsigned char* src_ = bptr[m] + (int64_t)(C_) * CK;                          \
+        const unsigned char* src_ = bptr[m] + (int64_t)(C_) * cstride;                     \
         _Pragma("unroll") for (int v = 0; v < V / 2; ++v)                                  \
-          breg[BUF_][m][v] = *reinterpret_cast<const u32x4*>(src_ + v * 16);               \
-        bscale[BUF_][m] = Sm[m][(int64_t)(brow / 128) * p.ks + ((C_) * CK + q * QB) / 128]; \
+          breg[BUF_][m][v] = load_stream(src_ + v * VSTEP);                                \
+        bscale[BUF_][m] = Sm[m][(int64_t)(brow / 128) * p.ks + ((C_) * CK) / 128];         \
       } else {                                                                             \
-        const unsigned char* src_ = bptr[m] + (int64_t)(C_) * CK * 2;                      \
+        const unsigned char* src_ = bptr[m] + (int64_t)(C_) * cstride;                     \
         _Pragma("unroll") for (int v = 0; v < V; ++v)                                      \
-          breg[BUF_][m][v] = *reinterpret_cast<const u32x4*>(src_ + v * 16);               \
+          breg[BUF_][m][v] = load_stream(src_ + v * VSTEP);                                \
       }                                                                                    \
     }                                                                                      \
   }
@@ -130,7 +166,7 @@ __global__ void __launch_bounds__(kThreads, MINW) stream_gemm_kernel(GroupedPara
     // compiler can count outstanding loads exactly and the weight prefetch
     // issued before the A store stays in flight.
     constexpr int PR = CK * 2 / 16;
-    u32x4 areg[A_PIECES];
+    u32x4 areg[2][A_PIECES];
     const unsigned char* a_row[A_PIECES];
 #pragma unroll
     for (int i = 0; i < A_PIECES; ++i) {
@@ -138,14 +174,14 @@ __global__ void __launch_bounds__(kThreads, MINW) stream_gemm_kernel(GroupedPara
       const int rr_ = min(m0 + c_ / PR, rows - 1);
       a_row[i] = reinterpret_cast<const unsigned char*>(A + (int64_t)rr_ * p.K) + (c_ % PR) * 16;
     }
-#define MOE_STREAM_LOAD_A(C_)                                                              \
+#define MOE_STREAM_LOAD_A(ABUF_, C_)                                                       \
     _Pragma("unroll") for (int i = 0; i < A_PIECES; ++i)                                   \
-      areg[i] = *reinterpret_cast<const u32x4*>(a_row[i] + (int64_t)(C_) * CK * 2);
-#define MOE_STREAM_STORE_A(BUF_)                                                           \
+      areg[ABUF_][i] = *reinterpret_cast<const u32x4*>(a_row[i] + (int64_t)(C_) * CK * 2);
+#define MOE_STREAM_STORE_A(ABUF_, BUF_)                                                    \
     _Pragma("unroll") for (int i = 0; i < A_PIECES; ++i) {                                 \
       const int c_ = tid + i * kThreads;                                                   \
       *reinterpret_cast<u32x4*>(lds_a + (BUF_) * MROWS * RS + (c_ / PR) * RS +             \
-                                (c_ % PR) * 16) = areg[i];                                 \
+                                (c_ % PR) * 16) = areg[ABUF_][i];                          \
     }
 
     f32x4 acc[NMAT][4];
@@ -158,11 +194,24 @@ __global__ void __launch_bounds__(kThreads, MINW) stream_gemm_kernel(GroupedPara
     // Loads are never skipped (chunk indices are clamped instead): branches
     // around loads would make the compiler's wait-count tracking fall back
     // to draining every outstanding load.
+    // Issue order per chunk: A rows, then weights.  Loads return in issue
+    // order, so storing A of chunk c + 1 (fetched a chunk earlier, ahead of
+    // its weights) waits for nothing newer: the weights of chunks c + 1 and
+    // c + 2 stay in flight across the barrier.
+#if MOE_SG_AHEAD
+    MOE_STREAM_LOAD_A(0, cb);
+    MOE_STREAM_LOAD_B(0, cb);
+    MOE_STREAM_LOAD_A(1, cb + min(1, NC - 1));
+    MOE_STREAM_LOAD_B(1, cb + min(1, NC - 1));
+    MOE_STREAM_STORE_A(0, 0);
+    MOE_BARRIER_LDS();
+#else
     MOE_STREAM_LOAD_B(0, cb);
     MOE_STREAM_LOAD_B(1, cb + min(1, NC - 1));
-    MOE_STREAM_LOAD_A(cb);
-    MOE_STREAM_STORE_A(0);
+    MOE_STREAM_LOAD_A(0, cb);
+    MOE_STREAM_STORE_A(0, 0);
     MOE_BARRIER_LDS();
+#endif
 
 #define MOE_STREAM_COMPUTE(BUF_)                                                           \
     {                                                                                      \
@@ -187,7 +236,7 @@ __global__ void __launch_bounds__(kThreads, MINW) stream_gemm_kernel(GroupedPara
         _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                    \
           if (SKIP && i >= mt) continue;                                                   \
           const u32x4 af = *reinterpret_cast<const u32x4*>(                                \
-              la_ + (i * 16 + (lane & 15)) * RS + (q * QB + s * 8) * 2);                   \
+              la_ + (i * 16 + (lane & 15)) * RS + koff(s) * 2);                             \
           _Pragma("unroll") for (int m = 0; m < NMAT; ++m)                                 \
             acc[m][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(                           \
                 __builtin_bit_cast(bf16x8_t, af), __builtin_bit_cast(bf16x8_t, bf[m]),     \
@@ -197,19 +246,33 @@ __global__ void __launch_bounds__(kThreads, MINW) stream_gemm_kernel(GroupedPara
     }
 
     for (int c = 0; c < NC; c += 2) {
+#if MOE_SG_AHEAD
       // even chunk: buffers 0
-      MOE_STREAM_LOAD_A(cb + min(c + 1, NC - 1));
       MOE_STREAM_COMPUTE(0);
+      MOE_STREAM_LOAD_A(0, cb + min(c + 2, NC - 1));
       MOE_STREAM_LOAD_B(0, cb + min(c + 2, NC - 1));
-      MOE_STREAM_STORE_A(1);
+      MOE_STREAM_STORE_A(1, 1);
       MOE_BARRIER_LDS();
       if (c + 1 >= NC) break;
       // odd chunk: buffers 1
-      MOE_STREAM_LOAD_A(cb + min(c + 2, NC - 1));
+      MOE_STREAM_COMPUTE(1);
+      MOE_STREAM_LOAD_A(1, cb + min(c + 3, NC - 1));
+      MOE_STREAM_LOAD_B(1, cb + min(c + 3, NC - 1));
+      MOE_STREAM_STORE_A(0, 0);
+      MOE_BARRIER_LDS();
+#else
+      MOE_STREAM_LOAD_A(0, cb + min(c + 1, NC - 1));
+      MOE_STREAM_COMPUTE(0);
+      MOE_STREAM_LOAD_B(0, cb + min(c + 2, NC - 1));
+      MOE_STREAM_STORE_A(0, 1);
+      MOE_BARRIER_LDS();
+      if (c + 1 >= NC) break;
+      MOE_STREAM_LOAD_A(0, cb + min(c + 2, NC - 1));
       MOE_STREAM_COMPUTE(1);
       MOE_STREAM_LOAD_B(1, cb + min(c + 3, NC - 1));
-      MOE_STREAM_STORE_A(0);
+      MOE_STREAM_STORE_A(0, 0);
       MOE_BARRIER_LDS();
+#endif
     }
 #undef MOE_STREAM_LOAD_A
 #undef MOE_STREAM_STORE_A
@@ -305,13 +368,15 @@ __global__ void __launch_bounds__(kThreads) splitk_reduce_kernel(GroupedParams p
 
 template <int BSRC, int EPI, int CK>
 moe_status launch_stream(const GroupedParams& p, hipStream_t stream) {
-  auto kern = stream_gemm_kernel<BSRC, EPI, CK, (EPI == EPI_SWIGLU ? MOE_SG_MINW : MOE_DN_MINW)>;
+  constexpr int MW = EPI == EPI_SWIGLU ? MOE_SG_MINW : MOE_DN_MINW;
+  auto kern = p.b_tiled ? stream_gemm_kernel<BSRC, EPI, CK, MW, true>
+                        : stream_gemm_kernel<BSRC, EPI, CK, MW, false>;
   constexpr size_t lds = 2 * 64 * (CK * 2 + 16);
-  static bool attr_set = false;
-  if (!attr_set) {
+  static bool attr_set[2] = {false, false};
+  if (!attr_set[p.b_tiled ? 1 : 0]) {
     MOE_CHECK_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                       (int)lds));
-    attr_set = true;
+    attr_set[p.b_tiled ? 1 : 0] = true;
   }
   const int ngroups = p.n_routed + (p.t_dense > 0 ? 1 : 0);
   const int out_cols = (EPI == EPI_SWIGLU) ? p.N / 2 : p.N;

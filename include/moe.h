@@ -50,6 +50,9 @@ typedef enum {
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
 typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_score;
 typedef enum { MOE_RELU = 0, MOE_GELU = 1, MOE_SWIGLU = 2 } moe_act;
+/* Layout of expert weight matrices: the [out, in] row-major layout of a
+ * linear layer, or the 16-row tiled layout moe_weight_tile produces. */
+typedef enum { MOE_W_ROWMAJOR = 0, MOE_W_TILED16 = 1 } moe_w_layout;
 
 #define MOE_MAX_EXPERTS 256
 #define MOE_MAX_TOPK 8
@@ -177,12 +180,17 @@ moe_status moe_bias_update(const int32_t* counts, float* b_select, int32_t E, in
  * Accumulation is fp32; the intermediate activation is stored in act_dtype.
  * max_rows bounds expert_off[e_end] - expert_off[e_begin] (host value; it
  * sizes the workspace and the grid; rows beyond it are a caller error).
+ * w_layout applies to all six weight matrices (w1, w3, w2, ws1, ws3, ws2);
+ * scales keep their layout.  MOE_W_TILED16 is supported with bf16 weights
+ * and, for fp8 weights, when the streaming path runs (max_rows <= 64 per
+ * executed expert and T_dense <= 64); otherwise MOE_ERR_UNSUPPORTED.
  */
 typedef struct moe_ffn_args {
   int32_t d, h, E, e_begin, e_end;
   int32_t act;            /* moe_act */
   int32_t act_dtype;      /* MOE_F32 or MOE_BF16 */
   int32_t w_dtype;        /* MOE_F32 (with f32 acts), MOE_BF16 or MOE_FP8_E4M3 */
+  int32_t w_layout;       /* moe_w_layout */
   int64_t max_rows;
   const void* x_send;     /* [*, d] */
   const int32_t* expert_off; /* [E + 1] */
@@ -207,6 +215,19 @@ typedef struct moe_ffn_args {
 size_t moe_ffn_workspace_bytes(const moe_ffn_args* a);
 moe_status moe_expert_ffn(const moe_ffn_args* a, void* workspace, size_t ws_bytes,
                           hipStream_t stream);
+
+/* One-time re-layout of weights for streaming: n_mats row-major matrices of
+ * `rows` rows of `row_bytes` bytes each (any dtype) are rewritten into the
+ * 16-row tiled layout.  Within matrix i, tile t holds rows [16t, 16t + 16)
+ * as row_bytes/64 consecutive 1 KB pieces; piece j holds bytes [64j, 64j + 64)
+ * of the tile's rows, the 16 bytes at 64j + 16q of row 16t + r at offset
+ * (16q + r) * 16.  This is the order in which a 64-lane wave feeding 16x16
+ * matrix-core fragments reads a weight tile, so streaming the tiled matrix is
+ * one contiguous read.  The matrices keep their sizes and their order;
+ * w_tiled must not overlap w.  Requires rows % 16 == 0, row_bytes % 64 == 0,
+ * 16-byte aligned pointers.  Computes nothing (a byte permutation). */
+moe_status moe_weight_tile(const void* w, void* w_tiled, int64_t n_mats, int32_t rows,
+                           int64_t row_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------- combine
  * Un-permute and weighted sum at the origin (Ultralytics, "How Tokens Move

@@ -115,3 +115,20 @@ def test_ffn_rejects_bad_arguments_before_launch():
 def test_combine_rejects_bad_arguments_before_launch():
     a = _abi.CombineArgs(T=4, d=100, k=2, e_begin=0, e_end=8, act_dtype=_abi.MOE_BF16)
     assert M.lib().moe_combine(C.byref(a), None) == _abi.MOE_ERR_INVALID
+
+
+def test_ffn_rejects_unknown_weight_layout():
+    a = _abi.FfnArgs(d=256, h=256, E=8, e_begin=0, e_end=8, act=_abi.MOE_SWIGLU,
+                     act_dtype=_abi.MOE_BF16, w_dtype=_abi.MOE_BF16, w_layout=5)
+    assert M.lib().moe_expert_ffn(C.byref(a), None, 0, None) == _abi.MOE_ERR_INVALID
+    assert b"w_layout" in M.lib().moe_last_error()
+
+
+def test_weight_tile_rejects_bad_arguments_before_launch():
+    L = M.lib()
+    assert L.moe_weight_tile(None, None, 1, 15, 64, None) == _abi.MOE_ERR_INVALID  # rows % 16
+    assert L.moe_weight_tile(None, None, 1, 16, 96, None) == _abi.MOE_ERR_INVALID  # row_bytes % 64
+    assert L.moe_weight_tile(None, None, 1, 16, 64, None) == _abi.MOE_ERR_INVALID  # null
+    assert L.moe_weight_tile(4096, 4096 + 512, 1, 16, 64, None) == _abi.MOE_ERR_INVALID  # overlap
+    assert b"overlaps" in L.moe_last_error()
+    assert L.moe_weight_tile(None, None, 0, 16, 64, None) == _abi.MOE_OK  # nothing to do
