@@ -43,8 +43,10 @@ constexpr int kThreads = kGemmThreads;
 #ifndef MOE_DN_SKIP
 #define MOE_DN_SKIP 0
 #endif
-// Weights are read exactly once per launch: nontemporal loads keep them from
-// displacing the activations in the caches and stream faster from HBM.
+// Weights are read exactly once per launch.  On the tiled layout every load
+// is a whole contiguous 1 KB piece, and nontemporal loads stream those
+// faster from HBM; on row-major rows (64-byte pieces of 16 rows per load)
+// they are slower, so they are used for tiles only.
 #ifndef MOE_SG_NT
 #define MOE_SG_NT 1
 #endif
@@ -59,9 +61,10 @@ constexpr int kThreads = kGemmThreads;
 #define MOE_SG_AHEAD 0
 #endif
 
+template <bool TL>
 __device__ __forceinline__ u32x4 load_stream(const unsigned char* ptr) {
   const u32x4* p = reinterpret_cast<const u32x4*>(ptr);
-  if constexpr (MOE_SG_NT) return __builtin_nontemporal_load(p);
+  if constexpr (TL && MOE_SG_NT) return __builtin_nontemporal_load(p);
   return *p;
 }
 
@@ -147,12 +150,12 @@ __global__ void __launch_bounds__(kThreads, MINW) stream_gemm_kernel(GroupedPara
       if constexpr (BSRC == B_FP8) {                                                       \
         const unsigned char* src_ = bptr[m] + (int64_t)(C_) * cstride;                     \
         _Pragma("unroll") for (int v = 0; v < V / 2; ++v)                                  \
-          breg[BUF_][m][v] = load_stream(src_ + v * VSTEP);                                \
+          breg[BUF_][m][v] = load_stream<TL>(src_ + v * VSTEP);                                \
         bscale[BUF_][m] = Sm[m][(int64_t)(brow / 128) * p.ks + ((C_) * CK) / 128];         \
       } else {                                                                             \
         const unsigned char* src_ = bptr[m] + (int64_t)(C_) * cstride;                     \
         _Pragma("unroll") for (int v = 0; v < V; ++v)                                      \
-          breg[BUF_][m][v] = load_stream(src_ + v * VSTEP);                                \
+          breg[BUF_][m][v] = load_stream<TL>(src_ + v * VSTEP);                                \
       }                                                                                    \
     }                                                                                      \
   }
