@@ -61,6 +61,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return u >> 16;
 }
 
+// Two floats -> packed bf16 with the hardware conversion (round to nearest
+// even, like f32_to_bf16 for finite values).
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+  typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
+  const bf16x2_hw v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }

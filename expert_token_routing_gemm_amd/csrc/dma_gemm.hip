@@ -17,11 +17,20 @@
 //    each wave waits for its own loads of a stage (vmcnt), then one
 //    workgroup barrier makes them visible.  The compiler does not track
 //    these waits, they are issued explicitly.
-//  * Every wave instruction fills 1 KB of LDS = 16 tile rows x 64 bytes.
-//    Inside a 1 KB block the four 16-byte chunks of row r are stored XOR-
-//    swizzled by h(r) = ((r >> 1) ^ (r >> 2)) & 3, so the MFMA fragment reads
-//    (consecutive rows, same chunk) hit distinct banks for 8- and 16-lane
-//    groups.
+//  * Every wave instruction fills 1 KB of LDS.  Row-major 16-bit operands:
+//    16 tile rows x 64 bytes, four consecutive lanes per row (full 64-byte
+//    global segments); inside the block the 16-byte chunks of row r are
+//    XOR-swizzled by h(r) = ((r >> 1) ^ (r >> 2)) & 3, so the MFMA fragment
+//    reads (consecutive rows, same chunk) hit distinct banks.  Tiled bf16
+//    weights: each stage of a 16-row tile is one contiguous 1 KB piece, which
+//    lands chunk-major (chunk c of row r at (16c + r) * 16), conflict-free
+//    without a swizzle.
+//  * fp8 weights: 32 rows x 32 bytes per 1 KB block (row-major: two lanes per
+//    row; tiled: two 512-byte chunk-major halves of 16 rows).  Each lane reads
+//    the 16 values of both k-steps of a stage at once, dequantises them with
+//    the block scale (hardware fp8 -> f32 conversion, scale, round to bf16)
+//    and feeds the bf16 MFMA.  Lane half h covers k [16h, 16h + 16) of a
+//    stage; the A fragments use the same k order.
 //  * Persistent grid with the same device-side tile table and XCD-aware
 //    tile order as grouped_gemm_kernel; SwiGLU pairs the w1 and w3 rows of
 //    the same output columns inside each wave.
@@ -36,10 +45,10 @@ constexpr int BKE = 32;      // k elements per stage (64 bytes of bf16)
 constexpr int NSTAGE = 4;    // LDS ring depth (loads run NSTAGE-1 stages ahead)
 constexpr int kGM = 4;       // m-tiles per strip
 
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
 #define MOE_GPTR(p) ((const void __attribute__((address_space(1)))*)(p))
 #define MOE_LPTR(p) ((void __attribute__((address_space(3)))*)(p))
-
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 
 // Waits until the global_load_lds of this wave for the current stage are
 // done (at most `ahead` later stages of LPW loads each still in flight) and
@@ -82,20 +91,24 @@ __device__ void scan_pairs_dma(int v0, int v1, int* out0, int* out1, int* total,
   *total = tot;
 }
 
-template <int EPI, int BM, int BN, int WM_, int WN_>
+template <int BSRC, bool TL, int EPI, int BM, int BN, int WM_, int WN_>
 __global__ void __launch_bounds__(64 * WM_ * WN_, 1) dma_gemm_kernel(GroupedParams p) {
+  constexpr bool F8 = BSRC == B_FP8;
   constexpr int NW = WM_ * WN_;                  // waves
   constexpr int kThreads = 64 * NW;
   constexpr int WTM = BM / WM_, WTN = BN / WN_;  // wave tile
   constexpr int QM = WTM / 32, QN = WTN / 32;    // 32x32 subtiles per wave
-  constexpr int STAGE_BYTES = (BM + BN) * BKE * 2;
-  constexpr int A_BLOCKS = BM / 16, B_BLOCKS = BN / 16;   // 1 KB blocks per stage
-  constexpr int LPW = (A_BLOCKS + B_BLOCKS) / NW;         // DMA instructions per wave per stage
+  constexpr int A_BYTES = BM * BKE * 2;
+  constexpr int B_BYTES = BN * BKE * (F8 ? 1 : 2);
+  constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  constexpr int A_BLOCKS = A_BYTES / 1024, B_BLOCKS = B_BYTES / 1024;  // 1 KB blocks per stage
+  constexpr int B_ROWS_PER_BLOCK = F8 ? 32 : 16;
+  constexpr int LPW = (A_BLOCKS + B_BLOCKS) / NW;  // DMA instructions per wave per stage
   static_assert((A_BLOCKS + B_BLOCKS) % NW == 0, "blocks split evenly over waves");
   static_assert(EPI != EPI_SWIGLU || QN % 2 == 0, "SwiGLU pairs subtiles");
   static_assert(2 * kThreads >= kMaxGroups + 1, "tile table needs two entries per thread");
   extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char* ring = smem;  // [NSTAGE][A 16 KB | B 16 KB]
+  unsigned char* ring = smem;  // [NSTAGE][A | B]
   int* s_tstart = reinterpret_cast<int*>(smem + NSTAGE * STAGE_BYTES);
   int* s_rows = s_tstart + (kMaxGroups + 1);
   int* s_r0 = s_rows + kMaxGroups;
@@ -138,13 +151,10 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, 1) dma_gemm_kernel(GroupedPara
   const int first = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
   const int a_sub = (p.a_shift && p.n_routed > 0) ? p.off[p.e_begin] : 0;
   const int c_sub = (p.c_shift && p.n_routed > 0) ? p.off[p.e_begin] : 0;
-  const int64_t stride = (int64_t)p.K * 2;  // bytes per row of A and B
+  const int64_t a_stride = (int64_t)p.K * 2;              // bytes per row of A
+  const int64_t b_stride = (int64_t)p.K * (F8 ? 1 : 2);   // bytes per row of B
+  const int64_t b_mat = p.b_stride * (F8 ? 1 : 2);        // bytes per expert matrix
   const int KT = p.K / BKE;
-
-  // DMA lane mapping inside a 1 KB block: position l -> row l/4, physical
-  // chunk l%4, logical chunk (l%4) ^ swz(l/4).
-  const int dr = lane >> 2;
-  const int dchunk = (lane & 3) ^ swz(dr);
 
   for (int tile = first; tile < total; tile += G) {
     int lo = 0, hi = ngroups - 1;
@@ -165,42 +175,74 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, 1) dma_gemm_kernel(GroupedPara
     const int m0 = m_t * BM;
 
     const unsigned char *A, *B1, *B3;
+    const float *S1 = nullptr, *S3 = nullptr;
     bf16_t* C;
     if (!dense) {
-      A = reinterpret_cast<const unsigned char*>(p.a_routed) + (int64_t)(s_r0[g] - a_sub) * stride;
+      A = reinterpret_cast<const unsigned char*>(p.a_routed) + (int64_t)(s_r0[g] - a_sub) * a_stride;
       C = reinterpret_cast<bf16_t*>(p.c_routed) + (int64_t)(s_r0[g] - c_sub) * p.ldc;
-      B1 = reinterpret_cast<const unsigned char*>(p.b1) + (int64_t)g * p.b_stride * 2;
-      B3 = p.b3 ? reinterpret_cast<const unsigned char*>(p.b3) + (int64_t)g * p.b_stride * 2 : B1;
+      B1 = reinterpret_cast<const unsigned char*>(p.b1) + (int64_t)g * b_mat;
+      B3 = p.b3 ? reinterpret_cast<const unsigned char*>(p.b3) + (int64_t)g * b_mat : B1;
+      if (F8) {
+        S1 = p.s1 + (int64_t)g * p.ns * p.ks;
+        S3 = p.s3 ? p.s3 + (int64_t)g * p.ns * p.ks : S1;
+      }
     } else {
       A = reinterpret_cast<const unsigned char*>(p.a_dense);
       C = reinterpret_cast<bf16_t*>(p.c_dense);
       B1 = reinterpret_cast<const unsigned char*>(p.bd1);
       B3 = p.bd3 ? reinterpret_cast<const unsigned char*>(p.bd3) : B1;
+      if (F8) {
+        S1 = p.sd1;
+        S3 = p.sd3 ? p.sd3 : S1;
+      }
     }
+    // weight row of B tile row tr (SwiGLU: each half of a wave column's rows
+    // is w1 or w3 of the same output columns)
+    auto b_row = [&](int tr, const unsigned char*& bm, const float*& sm) {
+      bm = B1;
+      sm = S1;
+      if (EPI == EPI_SWIGLU) {
+        const int col_wave = tr / WTN, rr = tr % WTN;
+        if (rr >= WTN / 2) {
+          bm = B3;
+          sm = S3;
+        }
+        return n_t * (BN / 2) + col_wave * (WTN / 2) + rr % (WTN / 2);
+      }
+      return n_t * BN + tr;
+    };
 
     // DMA instruction i of this wave fills 1 KB block b = wave + NW*i of the
-    // stage (A blocks first, then B blocks); lane -> tile row 16*(b mod
-    // blocks) + dr.  SwiGLU: each half of a wave column's B rows is w1 or w3
-    // of the same output columns.
+    // stage (A blocks first, then B blocks); LDS position l*16 <- lane l.
+    // src[i] is the stage-0 global address, kstep[i] the bytes per stage.
+    const int dr = lane >> 2;                      // row-major 16-bit: row
+    const int dchunk = (lane & 3) ^ swz(dr);       //   and logical chunk
     const unsigned char* src[LPW];
+    int kstep[LPW];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int b = wave + NW * i;
       if (b < A_BLOCKS) {
         const int ar = min(m0 + 16 * b + dr, rows - 1);
-        src[i] = A + (int64_t)ar * stride + dchunk * 16;
+        src[i] = A + (int64_t)ar * a_stride + dchunk * 16;
+        kstep[i] = BKE * 2;
       } else {
-        const int tr = 16 * (b - A_BLOCKS) + dr;  // B tile row
-        int brow;
-        const unsigned char* bm = B1;
-        if (EPI == EPI_SWIGLU) {
-          const int col_wave = tr / WTN, rr = tr % WTN;
-          bm = (rr >= WTN / 2) ? B3 : B1;
-          brow = n_t * (BN / 2) + col_wave * (WTN / 2) + rr % (WTN / 2);
+        int r_in;  // row inside the block
+        if (F8) r_in = TL ? 16 * (lane >> 5) + (lane & 15) : (lane >> 1);
+        else r_in = TL ? (lane & 15) : dr;
+        const int tr = B_ROWS_PER_BLOCK * (b - A_BLOCKS) + r_in;  // B tile row
+        const unsigned char* bm;
+        const float* sm;
+        const int brow = b_row(tr, bm, sm);
+        if (TL) {
+          // 16-row tile: 1 KB pieces of 64 bytes per row, in lane order
+          const int64_t tile_base = (int64_t)(brow >> 4) * 16 * b_stride;
+          src[i] = bm + tile_base + (F8 ? (lane & 31) : lane) * 16;
+          kstep[i] = F8 ? 512 : 1024;  // fp8: half kt%2 of piece kt/2
         } else {
-          brow = n_t * BN + tr;
+          src[i] = bm + (int64_t)brow * b_stride + (F8 ? (lane & 1) : dchunk) * 16;
+          kstep[i] = BKE * (F8 ? 1 : 2);
         }
-        src[i] = bm + (int64_t)brow * stride + dchunk * 16;
       }
     }
     auto issue = [&](int kt) {
@@ -208,10 +250,22 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, 1) dma_gemm_kernel(GroupedPara
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
         const int b = wave + NW * i;
-        __builtin_amdgcn_global_load_lds(MOE_GPTR(src[i] + (int64_t)kt * (BKE * 2)),
+        __builtin_amdgcn_global_load_lds(MOE_GPTR(src[i] + (int64_t)kt * kstep[i]),
                                          MOE_LPTR(st + b * 1024), 16, 0, 0);
       }
     };
+    // fp8 scales: one per B subtile and 128-k block (the subtile's 32
+    // weight rows lie in one 128-row block)
+    const float* sp[QN];
+    if constexpr (F8) {
+#pragma unroll
+      for (int j = 0; j < QN; ++j) {
+        const unsigned char* bm;
+        const float* sm;
+        const int brow = b_row(wn * WTN + j * 32, bm, sm);
+        sp[j] = sm + (int64_t)(brow >> 7) * p.ks;
+      }
+    }
 
     f32x16 acc[QM][QN];
 #pragma unroll
@@ -225,32 +279,59 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, 1) dma_gemm_kernel(GroupedPara
     for (int s = 0; s < NSTAGE - 1; ++s)
       if (s < KT) issue(s);
 
+    const int h = lane >> 5;  // k half of this lane: [16h, 16h + 16) of a stage
     for (int kt = 0; kt < KT; ++kt) {
+      float sc[QN];
+      if constexpr (F8) {
+#pragma unroll
+        for (int j = 0; j < QN; ++j) sc[j] = sp[j][kt >> 2];
+      }
       wait_stage_and_barrier<LPW>(min(NSTAGE - 2, KT - 1 - kt));
       if (kt + NSTAGE - 1 < KT) issue(kt + NSTAGE - 1);
       const unsigned char* st = ring + (kt % NSTAGE) * STAGE_BYTES;
+      u32x4 bq[QN][2];  // B fragments of both k-steps
+#pragma unroll
+      for (int j = 0; j < QN; ++j) {
+        const int R = wn * WTN + j * 32 + (lane & 31);  // B tile row
+        if constexpr (F8) {
+          const int boff = TL ? ((R >> 4) & 1) * 512 + (16 * h + (R & 15)) * 16
+                              : (R & 31) * 32 + h * 16;
+          const u32x4 w8 = *reinterpret_cast<const u32x4*>(st + A_BYTES + (R >> 5) * 1024 + boff);
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+            for (int wv = 0; wv < 2; ++wv) {
+              const uint32_t word = w8[2 * s2 + wv];
+              typedef float f2_t __attribute__((ext_vector_type(2)));
+              const f2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
+              const f2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
+              bq[j][s2][2 * wv] = bf16_pair(lo.x * sc[j], lo.y * sc[j]);
+              bq[j][s2][2 * wv + 1] = bf16_pair(hi.x * sc[j], hi.y * sc[j]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const int c = 2 * h + s2, r = R & 15;
+            const int boff = TL ? (16 * c + r) * 16 : (r * 4 + (c ^ swz(r))) * 16;
+            bq[j][s2] = *reinterpret_cast<const u32x4*>(st + A_BYTES + (R >> 4) * 1024 + boff);
+          }
+        }
+      }
 #pragma unroll
       for (int step = 0; step < BKE / 16; ++step) {
-        const int c = step * 2 + (lane >> 5);  // logical 16-byte chunk of this lane
-        u32x4 bfr[QN];
-#pragma unroll
-        for (int j = 0; j < QN; ++j) {
-          const int R = wn * WTN + j * 32 + (lane & 31);  // B tile row
-          const int r = R & 15;
-          bfr[j] = *reinterpret_cast<const u32x4*>(st + (A_BLOCKS + R / 16) * 1024 +
-                                                   (r * 4 + (c ^ swz(r))) * 16);
-        }
+        const int c = 2 * h + step;  // A chunk: k [16h + 8 step, +8)
 #pragma unroll
         for (int i = 0; i < QM; ++i) {
           const int R = wm * WTM + i * 32 + (lane & 31);  // A tile row
           const int r = R & 15;
           const u32x4 af =
-              *reinterpret_cast<const u32x4*>(st + (R / 16) * 1024 + (r * 4 + (c ^ swz(r))) * 16);
+              *reinterpret_cast<const u32x4*>(st + (R >> 4) * 1024 + (r * 4 + (c ^ swz(r))) * 16);
 #pragma unroll
           for (int j = 0; j < QN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8_t, af), __builtin_bit_cast(bf16x8_t, bfr[j]), acc[i][j],
-                0, 0, 0);
+                __builtin_bit_cast(bf16x8_t, af), __builtin_bit_cast(bf16x8_t, bq[j][step]),
+                acc[i][j], 0, 0, 0);
         }
       }
     }
@@ -286,10 +367,11 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, 1) dma_gemm_kernel(GroupedPara
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <int EPI, int BM, int BN, int WM_, int WN_>
+template <int BSRC, bool TL, int EPI, int BM, int BN, int WM_, int WN_>
 moe_status launch_dma(const GroupedParams& p, int64_t max_routed_rows, hipStream_t stream) {
-  auto kern = dma_gemm_kernel<EPI, BM, BN, WM_, WN_>;
-  constexpr size_t lds = NSTAGE * (BM + BN) * BKE * 2 + (3 * kMaxGroups + 1 + 4) * sizeof(int);
+  auto kern = dma_gemm_kernel<BSRC, TL, EPI, BM, BN, WM_, WN_>;
+  constexpr size_t lds = NSTAGE * (BM * 2 + BN * (BSRC == B_FP8 ? 1 : 2)) * BKE +
+                         (3 * kMaxGroups + 1 + 4) * sizeof(int);
   static bool attr_set = false;
   if (!attr_set) {
     MOE_CHECK_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -315,32 +397,45 @@ moe_status launch_dma(const GroupedParams& p, int64_t max_routed_rows, hipStream
 #ifndef MOE_DMA_BIG_WN
 #define MOE_DMA_BIG_WN 4
 #endif
-template <int EPI>
+template <int BSRC, bool TL, int EPI>
 moe_status launch_dma_shape(const GroupedParams& p, int64_t max_routed_rows, hipStream_t s) {
   const int groups = p.n_routed > 0 ? p.n_routed : 1;
   const bool small_groups = p.t_dense == 0 && max_routed_rows / groups < 768;
-  if (small_groups) return launch_dma<EPI, 128, 256, 1, 4>(p, max_routed_rows, s);
-  return launch_dma<EPI, 256, 256, 2, MOE_DMA_BIG_WN>(p, max_routed_rows, s);
+  if (small_groups) return launch_dma<BSRC, TL, EPI, 128, 256, 1, 4>(p, max_routed_rows, s);
+  return launch_dma<BSRC, TL, EPI, 256, 256, 2, MOE_DMA_BIG_WN>(p, max_routed_rows, s);
+}
+
+template <int BSRC, bool TL>
+moe_status launch_dma_epi(int epi, const GroupedParams& p, int64_t max_routed_rows,
+                          hipStream_t stream) {
+  switch (epi) {
+    case EPI_RELU:
+      return launch_dma_shape<BSRC, TL, EPI_RELU>(p, max_routed_rows, stream);
+    case EPI_GELU:
+      return launch_dma_shape<BSRC, TL, EPI_GELU>(p, max_routed_rows, stream);
+    case EPI_SWIGLU:
+      return launch_dma_shape<BSRC, TL, EPI_SWIGLU>(p, max_routed_rows, stream);
+    default:
+      return launch_dma_shape<BSRC, TL, EPI_NONE>(p, max_routed_rows, stream);
+  }
 }
 
 }  // namespace
 
-bool dma_gemm_supported(const GroupedParams& p, bool bf16_weights) {
-  return bf16_weights && p.N % 256 == 0 && p.K % BKE == 0;
+// bf16 or fp8 weights (row-major or tiled); output columns in whole 256-wide
+// tiles, K in whole 32-element stages (fp8: 128-element scale blocks).
+bool dma_gemm_supported(const GroupedParams& p, int bsrc) {
+  if (p.N % 256 != 0 || p.K % BKE != 0) return false;
+  return bsrc == B_SAME || (bsrc == B_FP8 && p.K % 128 == 0);
 }
 
-moe_status launch_dma_gemm(int epi, const GroupedParams& p, int64_t max_routed_rows,
+moe_status launch_dma_gemm(int bsrc, int epi, const GroupedParams& p, int64_t max_routed_rows,
                            hipStream_t stream) {
-  switch (epi) {
-    case EPI_RELU:
-      return launch_dma_shape<EPI_RELU>(p, max_routed_rows, stream);
-    case EPI_GELU:
-      return launch_dma_shape<EPI_GELU>(p, max_routed_rows, stream);
-    case EPI_SWIGLU:
-      return launch_dma_shape<EPI_SWIGLU>(p, max_routed_rows, stream);
-    default:
-      return launch_dma_shape<EPI_NONE>(p, max_routed_rows, stream);
-  }
+  if (bsrc == B_FP8)
+    return p.b_tiled ? launch_dma_epi<B_FP8, true>(epi, p, max_routed_rows, stream)
+                     : launch_dma_epi<B_FP8, false>(epi, p, max_routed_rows, stream);
+  return p.b_tiled ? launch_dma_epi<B_SAME, true>(epi, p, max_routed_rows, stream)
+                   : launch_dma_epi<B_SAME, false>(epi, p, max_routed_rows, stream);
 }
 
 }  // namespace moe

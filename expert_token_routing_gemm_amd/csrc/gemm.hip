@@ -559,20 +559,24 @@ moe_status run_ffn(const moe_ffn_args* a, const FfnPlan& pl, void* ws, hipStream
     if (st != MOE_OK) return st;
     if (mid_event) MOE_CHECK_HIP(hipEventRecord(mid_event, stream));
     st = launch_stream_gemm2_any(BSRC, p2, stream);
+  } else if (p1.b_tiled && (sizeof(AT) == 4 || !MOE_USE_DMA_GEMM || !dma_gemm_supported(p1, BSRC) ||
+                             !dma_gemm_supported(p2, BSRC))) {
+    set_error("moe_expert_ffn: tiled weights need bf16 activations and, off the streaming path, "
+              "h and d multiples of 256");
+    return MOE_ERR_UNSUPPORTED;
   } else if (sizeof(AT) == 4) {
     p1.ksplit = p2.ksplit = 1;
     st = launch_gemm1<AT, BSRC, 128, 128, 2, 2, 2>(a->act, p1, rows, stream);
     if (st != MOE_OK) return st;
     if (mid_event) MOE_CHECK_HIP(hipEventRecord(mid_event, stream));
     st = launch<AT, AT, BSRC, EPI_NONE, 128, 128, 2, 2, 2>(p2, rows, stream);
-  } else if (MOE_USE_DMA_GEMM && dma_gemm_supported(p1, BSRC == B_SAME) &&
-             dma_gemm_supported(p2, BSRC == B_SAME)) {
+  } else if (MOE_USE_DMA_GEMM && dma_gemm_supported(p1, BSRC) && dma_gemm_supported(p2, BSRC)) {
     p1.ksplit = p2.ksplit = 1;
     const int epi1 = a->act == MOE_RELU ? EPI_RELU : (a->act == MOE_GELU ? EPI_GELU : EPI_SWIGLU);
-    st = launch_dma_gemm(epi1, p1, rows, stream);
+    st = launch_dma_gemm(BSRC, epi1, p1, rows, stream);
     if (st != MOE_OK) return st;
     if (mid_event) MOE_CHECK_HIP(hipEventRecord(mid_event, stream));
-    st = launch_dma_gemm(EPI_NONE, p2, rows, stream);
+    st = launch_dma_gemm(BSRC, EPI_NONE, p2, rows, stream);
   } else {
     p1.ksplit = p2.ksplit = 1;
     st = launch_gemm1<AT, BSRC, MOE_BIG_BM, MOE_BIG_BN, 2, 2, MOE_BIG_MINB>(a->act, p1, rows, stream);
@@ -664,11 +668,6 @@ moe_status moe::expert_ffn_impl(const moe_ffn_args* a, void* ws, size_t ws_bytes
     return MOE_OK;
   }
   const FfnPlan pl = plan_ffn(a);
-  if (a->w_layout == MOE_W_TILED16 && !pl.small_m) {
-    set_error("moe_expert_ffn: tiled weights need the streaming path (bf16 activations, <= 64 "
-              "rows per executed expert, T_dense <= 64)");
-    return MOE_ERR_UNSUPPORTED;
-  }
   if (f32) return run_ffn<float, B_SAME>(a, pl, ws, stream, mid_event);
   if (fp8) return run_ffn<bf16_t, B_FP8>(a, pl, ws, stream, mid_event);
   return run_ffn<bf16_t, B_SAME>(a, pl, ws, stream, mid_event);

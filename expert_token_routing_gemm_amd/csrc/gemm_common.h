@@ -74,9 +74,9 @@ int stream_ck_for(bool swiglu, int K);
 moe_status launch_stream_gemm1_any(int bsrc, int act, const GroupedParams& p, hipStream_t s);
 moe_status launch_stream_gemm2_any(int bsrc, const GroupedParams& p, hipStream_t s);
 
-// Launcher of the LDS-DMA 256x256 bf16 kernel (dma_gemm.hip).
-bool dma_gemm_supported(const GroupedParams& p, bool bf16_weights);
-moe_status launch_dma_gemm(int epi, const GroupedParams& p, int64_t max_routed_rows,
+// Launcher of the LDS-DMA grouped kernel for bf16 and fp8 weights (dma_gemm.hip).
+bool dma_gemm_supported(const GroupedParams& p, int bsrc);
+moe_status launch_dma_gemm(int bsrc, int epi, const GroupedParams& p, int64_t max_routed_rows,
                            hipStream_t stream);
 
 }  // namespace moe

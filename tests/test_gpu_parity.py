@@ -209,9 +209,14 @@ def test_weight_tile_layout():
 
 
 TILED = {
+    # streaming path
     "c1-small": (1, dict(T=40, d=512, h=768)),
     "c1-tiny-ragged": (1, dict(T=5, d=256, h=384)),
     "c4-decode": (4, dict(T=48, d=512, h=256)),
+    # LDS-DMA path: bf16 and fp8 weights, 128- and 256-row tiles
+    "c2-small": (2, dict(T=1000, d=512, h=640)),
+    "c3-small": (3, dict(T=4096, d=256, h=512)),
+    "c4-small": (4, dict(T=256, d=512, h=256)),
 }
 
 
@@ -237,10 +242,11 @@ def test_tiled_weights_full_decode(c1):
     np.testing.assert_array_equal(g_t["y"], g_r["y"])
 
 
-def test_tiled_weights_rejected_off_streaming_path():
+def test_tiled_weights_rejected_where_unsupported():
+    """fp32 activations have no tiled-weight kernel: a clear error, no launch."""
     from expert_token_routing_gemm_amd import MoEError
-    wl = make_workload(2, T=2048, d=256, h=256)
-    with pytest.raises(MoEError):
+    wl = make_workload(0, T=512, d=256, h=256)
+    with pytest.raises(MoEError, match="tiled"):
         run_layer(wl, w_layout=1)
 
 
