@@ -14,7 +14,7 @@
 //   hist_kernel      : block b owns a chunk of TB tokens (TB*k <= 256
 //                      assignments); LDS-private histogram -> blk[b][e].
 //   scan_kernel      : one workgroup; per expert an exclusive scan over blocks
-//                      (in place in blk, split over up to 64 lanes), counts,
+//                      (blk -> base, split over kScanThreads / E chunks), counts,
 //                      kept = min(counts, C), the expert offsets by a
 //                      wave-level scan, per-rank counts.
 //   rank_pack_kernel : recomputes each assignment's position: block base +
@@ -46,55 +46,67 @@ __global__ void __launch_bounds__(kThreads) hist_kernel(const int32_t* __restric
   for (int e = threadIdx.x; e < E; e += kThreads) blk[(int64_t)blockIdx.x * E + e] = cnt[e];
 }
 
-// scan_kernel: one workgroup of kScanThreads.  Expert e owns P consecutive
-// threads (P = largest power of two <= min(64, kScanThreads / E), so they are
-// lanes of one wave); thread p of expert e sums a contiguous chunk of the
-// per-block counts, a segmented wave scan turns the chunk sums into chunk
-// bases, and a second pass over the chunk writes each block's exclusive base
-// in place.  Loads of a chunk are independent, so the serial depth is the
-// chunk length (nblocks / P), not nblocks.
+// scan_kernel: one workgroup of kScanThreads.  Thread (p, e) = (tid / E,
+// tid % E) owns expert e on the p-th of P = kScanThreads / E contiguous
+// block chunks, so the lanes of a wave read consecutive experts of a block
+// (coalesced).  Chunk sums meet in LDS, each thread adds the sums of the
+// earlier chunks of its expert, and a second pass writes every block's
+// exclusive base (to a separate array, so all loads of a pass are
+// independent and G of them are in flight per thread).
 constexpr int kScanThreads = 1024;
 
 __global__ void __launch_bounds__(kScanThreads) scan_kernel(
-    int32_t* __restrict__ blk, int nblocks, int E, int R, int C, int P, int32_t* __restrict__ counts,
-    int32_t* __restrict__ kept, int32_t* __restrict__ off, int32_t* __restrict__ rank_counts,
-    int32_t* __restrict__ rank_off) {
+    const int32_t* __restrict__ blk, int32_t* __restrict__ base, int nblocks, int E, int R, int C,
+    int32_t* __restrict__ counts, int32_t* __restrict__ kept, int32_t* __restrict__ off,
+    int32_t* __restrict__ rank_counts, int32_t* __restrict__ rank_off) {
+  constexpr int G = 32;  // independent loads in flight per thread
+  __shared__ int part[kScanThreads];  // [P][E] chunk sums
   __shared__ int tot[MOE_MAX_EXPERTS];
   __shared__ int wsum[MOE_MAX_EXPERTS / 64];
   __shared__ int sh_off[MOE_MAX_EXPERTS + 1];
   const int tid = threadIdx.x;
   const int lane = lane_id();
-  const int e = tid / P;
-  const int p = tid - e * P;
+  const int P = kScanThreads / E;
+  const int e = tid % E;
+  const int p = tid / E;
+  const bool active = p < P;
   const int chunk = (nblocks + P - 1) / P;
   const int b0 = min(p * chunk, nblocks);
-  const int b1 = min(b0 + chunk, nblocks);
+  const int b1 = active ? min(b0 + chunk, nblocks) : b0;
   int sum = 0;
-  if (e < E) {
+  {
     int b = b0;
-    for (; b + 8 <= b1; b += 8) {
-      int v[8];
+    for (; b + G <= b1; b += G) {
+      int v[G];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = blk[(int64_t)(b + i) * E + e];
+      for (int i = 0; i < G; ++i) v[i] = blk[(int64_t)(b + i) * E + e];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sum += v[i];
+      for (int i = 0; i < G; ++i) sum += v[i];
     }
     for (; b < b1; ++b) sum += blk[(int64_t)b * E + e];
   }
-  // segmented inclusive scan over the P lanes of the expert
-  int incl = sum;
-  for (int o = 1; o < P; o <<= 1) {
-    const int u = __shfl_up(incl, o, 64);
-    if ((lane & (P - 1)) >= o) incl += u;
-  }
-  if (e < E) {
-    int run = incl - sum;
-    for (int b = b0; b < b1; ++b) {
+  if (active) part[p * E + e] = sum;
+  __syncthreads();
+  if (active) {
+    int run = 0;
+    for (int q = 0; q < p; ++q) run += part[q * E + e];
+    if (p == P - 1) tot[e] = run + sum;
+    int b = b0;
+    for (; b + G <= b1; b += G) {
+      int v[G];
+#pragma unroll
+      for (int i = 0; i < G; ++i) v[i] = blk[(int64_t)(b + i) * E + e];
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        base[(int64_t)(b + i) * E + e] = run;
+        run += v[i];
+      }
+    }
+    for (; b < b1; ++b) {
       const int v = blk[(int64_t)b * E + e];
-      blk[(int64_t)b * E + e] = run;
+      base[(int64_t)b * E + e] = run;
       run += v;
     }
-    if (p == P - 1) tot[e] = incl;
   }
   __syncthreads();
   // exclusive scan of kept over the experts (threads 0..255)
@@ -128,12 +140,6 @@ __global__ void __launch_bounds__(kScanThreads) scan_kernel(
     rank_off[r] = sh_off[r * per];
   }
   if (tid == 0) rank_off[R] = sh_off[E];
-}
-
-int scan_lanes(int E) {
-  int P = 64;
-  while (P > 1 && P * E > kScanThreads) P >>= 1;
-  return P;
 }
 
 template <int UNROLL>
@@ -403,7 +409,7 @@ extern "C" int64_t moe_send_rows_max(int64_t T, int32_t k, int32_t E, int32_t ca
 extern "C" size_t moe_dispatch_workspace_bytes(const moe_dispatch_args* a) {
   if (!a || a->T <= 0 || a->k <= 0 || a->T * a->k <= kSmallAssign) return 0;
   const Plan p = plan_for(a->T, a->k);
-  return align_up((size_t)p.nblocks * a->E * sizeof(int32_t), 256);
+  return 2 * align_up((size_t)p.nblocks * a->E * sizeof(int32_t), 256);
 }
 
 extern "C" moe_status moe_dispatch(const moe_dispatch_args* a, void* ws, size_t ws_bytes,
@@ -441,18 +447,19 @@ extern "C" moe_status moe_dispatch(const moe_dispatch_args* a, void* ws, size_t 
     return MOE_OK;
   }
   int32_t* blk = static_cast<int32_t*>(ws);
+  int32_t* bases = blk + align_up((size_t)p.nblocks * a->E * sizeof(int32_t), 256) / sizeof(int32_t);
   if (a->T > 0) {
     hist_kernel<<<p.nblocks, kThreads, 0, stream>>>(a->ids, blk, a->T * a->k,
                                                      p.tokens_per_block * a->k, a->E);
     MOE_CHECK_LAUNCH();
   }
-  scan_kernel<<<1, kScanThreads, 0, stream>>>(blk, a->T > 0 ? p.nblocks : 0, a->E, a->R,
-                                              a->capacity, scan_lanes(a->E), a->counts, a->kept,
-                                              a->expert_off, a->rank_counts, a->rank_off);
+  scan_kernel<<<1, kScanThreads, 0, stream>>>(blk, bases, a->T > 0 ? p.nblocks : 0, a->E, a->R,
+                                              a->capacity, a->counts, a->kept, a->expert_off,
+                                              a->rank_counts, a->rank_off);
   MOE_CHECK_LAUNCH();
   if (a->T > 0) {
     rank_pack_kernel<4><<<p.nblocks, kThreads, 0, stream>>>(
-        a->ids, blk, a->expert_off, (const u32x4*)a->x, a->slot, a->src, (u32x4*)a->x_send, a->T,
+        a->ids, bases, a->expert_off, (const u32x4*)a->x, a->slot, a->src, (u32x4*)a->x_send, a->T,
         a->k, a->E, a->capacity, p.tokens_per_block, row16);
     MOE_CHECK_LAUNCH();
   }

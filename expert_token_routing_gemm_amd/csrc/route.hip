@@ -144,6 +144,9 @@ __device__ void finish_token_small(const float* L, int E, int k, int score, int 
 }
 
 // ---------------------------------------------------------------- E <= 8 fused
+#ifndef MOE_RS_TPW
+#define MOE_RS_TPW 4  // tokens per wave in flight
+#endif
 // Block = 4 waves; each wave owns TPW tokens at a time.  Lane l covers the
 // 16-byte chunks l, l+64, ... of a row (coalesced 128-bit loads of x).
 template <typename T, int TPW, bool WR_LDS>
@@ -591,7 +594,7 @@ extern "C" moe_status moe_route(const moe_route_args* a, void* ws, size_t ws_byt
     const bool stage = a->T > 1024;
     const size_t lds = stage ? (size_t)a->E * a->d * (a->act_dtype == MOE_F32 ? 4 : 2) : 0;
     if (stage) {
-      constexpr int TPW = 4;
+      constexpr int TPW = MOE_RS_TPW;
       const int grid = (int)std::min<int64_t>((a->T + 4 * TPW - 1) / (4 * TPW),
                                               (int64_t)device_info().cus * 2);
       if (a->act_dtype == MOE_F32) {
