@@ -7,13 +7,14 @@
 // Design (MI355X-specific):
 //  * 256x256 output tile per workgroup of 8 waves (2 per SIMD); each wave
 //    owns 128x64 as 4x2 v_mfma_f32_32x32x16_bf16 subtiles (the full-rate bf16
-//    MFMA on gfx950; 128 fp32 accumulators per lane in AGPRs).  Per k the
-//    workgroup reads 8*(128+64)*2 bytes of LDS and writes 512*2 by DMA for
-//    2*256*256 flops, about 0.03 B/flop: within LDS bandwidth at the MFMA
-//    peak, where 64x64 wave tiles are not.  Groups of a few hundred rows use
-//    128x256 tiles (4 waves of 128x64) to pad less.
+//    MFMA on gfx950; 128 fp32 accumulators per lane).  Per k the workgroup
+//    reads 8*(128+64)*2 bytes of LDS and writes 512*2 by DMA for 2*256*256
+//    flops, about 0.03 B/flop: within LDS bandwidth at the MFMA peak, where
+//    64x64 wave tiles are not.  Groups of a few hundred rows and fp8 weights
+//    use 128x256 tiles (4 waves of 128x64), two workgroups per CU.
 //  * Global -> LDS with global_load_lds_dwordx4 (no register staging): a
-//    4-stage ring of 32-k stages (32 KB each), filled three stages ahead;
+//    ring of 32-k stages (4 stages of 32 KB for 256x256, 3 of 24 KB for
+//    128x256), filled NS-1 stages ahead;
 //    each wave waits for its own loads of a stage (vmcnt), then one
 //    workgroup barrier makes them visible.  The compiler does not track
 //    these waits, they are issued explicitly.
@@ -91,8 +92,10 @@ __device__ void scan_pairs_dma(int v0, int v1, int* out0, int* out1, int* total,
   *total = tot;
 }
 
-template <int BSRC, bool TL, int EPI, int BM, int BN, int WM_, int WN_>
-__global__ void __launch_bounds__(64 * WM_ * WN_, 1) dma_gemm_kernel(GroupedParams p) {
+// NS: LDS ring depth (loads run NS-1 stages ahead); MINW: waves per SIMD the
+// register budget must allow (2 with 4-wave workgroups = two per CU).
+template <int BSRC, bool TL, int EPI, int BM, int BN, int WM_, int WN_, int NS, int MINW>
+__global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedParams p) {
   constexpr bool F8 = BSRC == B_FP8;
   constexpr int NW = WM_ * WN_;                  // waves
   constexpr int kThreads = 64 * NW;
@@ -108,8 +111,8 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, 1) dma_gemm_kernel(GroupedPara
   static_assert(EPI != EPI_SWIGLU || QN % 2 == 0, "SwiGLU pairs subtiles");
   static_assert(2 * kThreads >= kMaxGroups + 1, "tile table needs two entries per thread");
   extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char* ring = smem;  // [NSTAGE][A | B]
-  int* s_tstart = reinterpret_cast<int*>(smem + NSTAGE * STAGE_BYTES);
+  unsigned char* ring = smem;  // [NS][A | B]
+  int* s_tstart = reinterpret_cast<int*>(smem + NS * STAGE_BYTES);
   int* s_rows = s_tstart + (kMaxGroups + 1);
   int* s_r0 = s_rows + kMaxGroups;
   int* s_scan = s_r0 + kMaxGroups;
@@ -246,7 +249,7 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, 1) dma_gemm_kernel(GroupedPara
       }
     }
     auto issue = [&](int kt) {
-      unsigned char* st = ring + (kt % NSTAGE) * STAGE_BYTES;
+      unsigned char* st = ring + (kt % NS) * STAGE_BYTES;
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
         const int b = wave + NW * i;
@@ -276,7 +279,7 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, 1) dma_gemm_kernel(GroupedPara
     // every wave has finished reading the ring of the previous tile
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-    for (int s = 0; s < NSTAGE - 1; ++s)
+    for (int s = 0; s < NS - 1; ++s)
       if (s < KT) issue(s);
 
     const int h = lane >> 5;  // k half of this lane: [16h, 16h + 16) of a stage
@@ -286,9 +289,9 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, 1) dma_gemm_kernel(GroupedPara
 #pragma unroll
         for (int j = 0; j < QN; ++j) sc[j] = sp[j][kt >> 2];
       }
-      wait_stage_and_barrier<LPW>(min(NSTAGE - 2, KT - 1 - kt));
-      if (kt + NSTAGE - 1 < KT) issue(kt + NSTAGE - 1);
-      const unsigned char* st = ring + (kt % NSTAGE) * STAGE_BYTES;
+      wait_stage_and_barrier<LPW>(min(NS - 2, KT - 1 - kt));
+      if (kt + NS - 1 < KT) issue(kt + NS - 1);
+      const unsigned char* st = ring + (kt % NS) * STAGE_BYTES;
       u32x4 bq[QN][2];  // B fragments of both k-steps
 #pragma unroll
       for (int j = 0; j < QN; ++j) {
@@ -367,11 +370,14 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, 1) dma_gemm_kernel(GroupedPara
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <int BSRC, bool TL, int EPI, int BM, int BN, int WM_, int WN_>
+template <int BSRC, bool TL, int EPI, int BM, int BN, int WM_, int WN_, int NS = NSTAGE,
+          int MINW = 1>
 moe_status launch_dma(const GroupedParams& p, int64_t max_routed_rows, hipStream_t stream) {
-  auto kern = dma_gemm_kernel<BSRC, TL, EPI, BM, BN, WM_, WN_>;
-  constexpr size_t lds = NSTAGE * (BM * 2 + BN * (BSRC == B_FP8 ? 1 : 2)) * BKE +
+  auto kern = dma_gemm_kernel<BSRC, TL, EPI, BM, BN, WM_, WN_, NS, MINW>;
+  constexpr int per_cu = MINW * 4 / (WM_ * WN_) > 0 ? MINW * 4 / (WM_ * WN_) : 1;  // workgroups
+  constexpr size_t lds = NS * (BM * 2 + BN * (BSRC == B_FP8 ? 1 : 2)) * BKE +
                          (3 * kMaxGroups + 1 + 4) * sizeof(int);
+  static_assert(per_cu * lds <= 160 * 1024, "LDS of the resident workgroups");
   static bool attr_set = false;
   if (!attr_set) {
     MOE_CHECK_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -384,7 +390,7 @@ moe_status launch_dma(const GroupedParams& p, int64_t max_routed_rows, hipStream
                              (p.t_dense > 0 ? (p.t_dense + BM - 1) / BM : 0);
   const int64_t tiles_ub = m_tiles_ub * nt;
   if (ngroups == 0 || tiles_ub == 0) return MOE_OK;
-  int64_t grid = device_info().cus;
+  int64_t grid = (int64_t)device_info().cus * per_cu;
   if (grid > tiles_ub) grid = tiles_ub;
   if (grid >= 8) grid = grid / 8 * 8;
   kern<<<(int)grid, 64 * WM_ * WN_, lds, stream>>>(p);
@@ -392,16 +398,23 @@ moe_status launch_dma(const GroupedParams& p, int64_t max_routed_rows, hipStream
   return MOE_OK;
 }
 
-// Tile shapes: 256x256 with 2x4 waves of 128x64 for large groups; 128-row
-// tiles for groups of a few hundred rows (less padding).
+// Tile shapes: 256x256 with 2x4 waves of 128x64 (one workgroup per CU) for
+// large bf16 groups; 128x256 tiles of 4 waves, two workgroups per CU with a
+// 3-stage ring each, for groups of a few hundred rows (less padding, and one
+// workgroup's prologue and epilogue overlap the other's main loop) and for
+// fp8 weights (their B stage is half as large, so the second workgroup's
+// extra operand traffic costs less).  Measured: Switch workload 1.00 ->
+// 0.87 ms, DeepSeek-V3 share 1.78 -> 1.67 ms; the bf16 prefill workload stays
+// faster on 256x256 (11.8 vs 13.0 ms).
 #ifndef MOE_DMA_BIG_WN
 #define MOE_DMA_BIG_WN 4
 #endif
 template <int BSRC, bool TL, int EPI>
 moe_status launch_dma_shape(const GroupedParams& p, int64_t max_routed_rows, hipStream_t s) {
   const int groups = p.n_routed > 0 ? p.n_routed : 1;
-  const bool small_groups = p.t_dense == 0 && max_routed_rows / groups < 768;
-  if (small_groups) return launch_dma<BSRC, TL, EPI, 128, 256, 1, 4>(p, max_routed_rows, s);
+  const bool small_tiles =
+      BSRC == B_FP8 || (p.t_dense == 0 && max_routed_rows / groups < 768);
+  if (small_tiles) return launch_dma<BSRC, TL, EPI, 128, 256, 1, 4, 3, 2>(p, max_routed_rows, s);
   return launch_dma<BSRC, TL, EPI, 256, 256, 2, MOE_DMA_BIG_WN>(p, max_routed_rows, s);
 }
 
