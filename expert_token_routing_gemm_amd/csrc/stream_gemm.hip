@@ -82,6 +82,7 @@ __global__ void __launch_bounds__(kThreads, MINW) stream_gemm_kernel(GroupedPara
   constexpr bool IL = MOE_SG_IL || TL;
   static_assert(A_PIECES >= 1, "chunk too small");
   static_assert(BSRC != B_FP8 || CK <= 128, "one fp8 scale block per chunk");
+  static_assert(BSRC != B_FP8 || CK >= 64, "fp8 chunks hold whole 16-byte loads per lane");
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* lds_a = smem;  // [2][MROWS][RS]
 
@@ -425,7 +426,8 @@ namespace {
 
 template <int BSRC, int EPI>
 moe_status launch_stream_k(const GroupedParams& p, hipStream_t s) {
-  constexpr int CK = EPI == EPI_SWIGLU ? MOE_SG_CK : MOE_DN_CK;
+  constexpr int CK0 = EPI == EPI_SWIGLU ? MOE_SG_CK : MOE_DN_CK;
+  constexpr int CK = (BSRC == B_FP8 && CK0 < 64) ? 64 : CK0;
   if (p.K % CK == 0) return launch_stream<BSRC, EPI, CK>(p, s);
   return launch_stream<BSRC, EPI, 128>(p, s);
 }
