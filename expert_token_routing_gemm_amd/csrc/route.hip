@@ -46,23 +46,27 @@ struct Vec16;  // 16 bytes of T, widened to floats
 template <>
 struct Vec16<float> {
   static constexpr int N = 4;
+  __device__ __forceinline__ static void widen(u32x4 v, float* out) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(v[i]);
+  }
   __device__ __forceinline__ static void load(const void* p, float* out) {
-    const float4 v = *reinterpret_cast<const float4*>(p);
-    out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+    widen(*reinterpret_cast<const u32x4*>(p), out);
   }
 };
 
 template <>
 struct Vec16<bf16_t> {
   static constexpr int N = 8;
-  __device__ __forceinline__ static void load(const void* p, float* out) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  __device__ __forceinline__ static void widen(u32x4 v, float* out) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      out[2 * i] = __uint_as_float(w[i] << 16);
-      out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+      out[2 * i] = __uint_as_float(v[i] << 16);
+      out[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
     }
+  }
+  __device__ __forceinline__ static void load(const void* p, float* out) {
+    widen(*reinterpret_cast<const u32x4*>(p), out);
   }
 };
 
@@ -178,18 +182,22 @@ __global__ void __launch_bounds__(256) route_small_kernel(
     for (int i = 0; i < TPW; ++i)
 #pragma unroll
       for (int e = 0; e < EMAX; ++e) acc[i][e] = 0.f;
+    // x chunks are fetched one step ahead (clamped index, so the loads are
+    // unconditional): the next chunk is in flight while this one is used.
+    u32x4 nxt[TPW];
+    auto fetch = [&](int c_) {
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        const int64_t t = min(t0 + i, T_tok - 1);
+        nxt[i] = *reinterpret_cast<const u32x4*>(x + t * d + (int64_t)c_ * VN);
+      }
+    };
+    fetch(min(lane, nchunk - 1));
     for (int c = lane; c < nchunk; c += kWave) {
       float xv[TPW][VN];
 #pragma unroll
-      for (int i = 0; i < TPW; ++i) {
-        const int64_t t = t0 + i;
-        if (t < T_tok) {
-          Vec16<T>::load(x + t * d + (int64_t)c * VN, xv[i]);
-        } else {
-#pragma unroll
-          for (int v = 0; v < VN; ++v) xv[i][v] = 0.f;
-        }
-      }
+      for (int i = 0; i < TPW; ++i) Vec16<T>::widen(nxt[i], xv[i]);
+      fetch(min(c + kWave, nchunk - 1));
 #pragma unroll
       for (int e = 0; e < EMAX; ++e) {
         if (e < E) {
