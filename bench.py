@@ -67,8 +67,11 @@ class Events:
             self.hip.hipEventDestroy(e)
 
 
-def algorithmic_bytes(wl, kept_rows: int, used_experts: int, shared: bool):
-    """Bytes each stage must move (read once, write once), per launch."""
+def algorithmic_bytes(wl, kept_rows: int, used_experts: int, shared: bool, sent_rows=None):
+    """Bytes each stage must move (read once, write once), per launch.
+    kept_rows: rows of the executed experts; sent_rows: rows of the whole
+    send buffer the dispatch packs (all ranks' segments)."""
+    sent = kept_rows if sent_rows is None else sent_rows
     sa = 4 if wl.act_dtype == "f32" else 2
     sw = {"f32": 4, "bf16": 2, "fp8": 1}[wl.w_dtype]
     T, d, h, E, k = wl.T, wl.d, wl.h, wl.E, wl.k
@@ -77,7 +80,7 @@ def algorithmic_bytes(wl, kept_rows: int, used_experts: int, shared: bool):
     groups = used_experts + (1 if shared else 0)
     return {
         "route": T * d * sa + E * d * sa + 8 * T * k,
-        "dispatch": 8 * T * k + 4 * kept_rows + T * d * sa + kept_rows * d * sa,
+        "dispatch": 8 * T * k + 4 * sent + T * d * sa + sent * d * sa,
         "gemm1": n1 * h * d * sw * groups + nx * d * sa + nx * h * sa,
         "gemm2": d * h * sw * groups + nx * h * sa + nx * d * sa,
         "combine": kept_rows * d * sa + 2 * T * d * sa + (T * d * sa if shared else 0) + 8 * T * k,
@@ -224,7 +227,7 @@ def main():
     kept_rows = int(off[wl.e_end] - off[wl.e_begin])
     used = int(np.count_nonzero(res["kept"][wl.e_begin:wl.e_end]))
     shared = wl.shared is not None
-    nbytes = algorithmic_bytes(wl, kept_rows, used, shared)
+    nbytes = algorithmic_bytes(wl, kept_rows, used, shared, sent_rows=int(off[wl.E]))
     flops = gemm_flops(wl, kept_rows, shared)
     # the dominant kernel: the first expert GEMM (streams w1 and w3)
     g1_s = stage_ms["gemm1"] / 1e3

@@ -94,7 +94,11 @@ __device__ void scan_pairs_dma(int v0, int v1, int* out0, int* out1, int* total,
 
 // NS: LDS ring depth (loads run NS-1 stages ahead); MINW: waves per SIMD the
 // register budget must allow (2 with 4-wave workgroups = two per CU).
-template <int BSRC, bool TL, int EPI, int BM, int BN, int WM_, int WN_, int NS, int MINW>
+// PART: split-K into p.ksplit slices, each writing fp32 partial sums
+// [slice][row][col] (row = partial row as in GroupedParams) with no
+// activation; the caller reduces the slices in a fixed order.
+template <int BSRC, bool TL, int EPI, int BM, int BN, int WM_, int WN_, int NS, int MINW,
+          bool PART>
 __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedParams p) {
   constexpr bool F8 = BSRC == B_FP8;
   constexpr int NW = WM_ * WN_;                  // waves
@@ -157,9 +161,13 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
   const int64_t a_stride = (int64_t)p.K * 2;              // bytes per row of A
   const int64_t b_stride = (int64_t)p.K * (F8 ? 1 : 2);   // bytes per row of B
   const int64_t b_mat = p.b_stride * (F8 ? 1 : 2);        // bytes per expert matrix
-  const int KT = p.K / BKE;
+  const int KS = PART ? p.ksplit : 1;
+  const int KT = p.K / BKE / KS;  // stages of one K slice
 
-  for (int tile = first; tile < total; tile += G) {
+  for (int work = first; work < total * KS; work += G) {
+    const int z = work / total;  // K slice (consecutive work items share it)
+    const int tile = work - z * total;
+    const int kbase = z * KT;
     int lo = 0, hi = ngroups - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -248,6 +256,8 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
         }
       }
     }
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) src[i] += (int64_t)kbase * kstep[i];
     auto issue = [&](int kt) {
       unsigned char* st = ring + (kt % NS) * STAGE_BYTES;
 #pragma unroll
@@ -287,7 +297,7 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
       float sc[QN];
       if constexpr (F8) {
 #pragma unroll
-        for (int j = 0; j < QN; ++j) sc[j] = sp[j][kt >> 2];
+        for (int j = 0; j < QN; ++j) sc[j] = sp[j][(kbase + kt) >> 2];
       }
       wait_stage_and_barrier<LPW>(min(NS - 2, KT - 1 - kt));
       if (kt + NS - 1 < KT) issue(kt + NS - 1);
@@ -341,6 +351,22 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
 
     // epilogue: value v of a lane is row 8*(v/4) + 4*(lane/32) + v%4,
     // column lane%32 of its 32x32 subtile
+    if constexpr (PART) {
+      const int64_t prow0 =
+          dense ? p.max_rows : (int64_t)(s_r0[g] - (p.n_routed > 0 ? p.off[p.e_begin] : 0));
+#pragma unroll
+      for (int i = 0; i < QM; ++i) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = m0 + wm * WTM + i * 32 + 8 * (v / 4) + 4 * (lane >> 5) + (v % 4);
+          if (row >= rows) continue;
+          float* prow = p.partial + ((int64_t)z * p.prow_total + prow0 + row) * p.ldc;
+#pragma unroll
+          for (int j = 0; j < QN; ++j) prow[n_t * BN + wn * WTN + j * 32 + (lane & 31)] = acc[i][j][v];
+        }
+      }
+      continue;
+    }
 #pragma unroll
     for (int i = 0; i < QM; ++i) {
 #pragma unroll
@@ -371,9 +397,9 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
 }
 
 template <int BSRC, bool TL, int EPI, int BM, int BN, int WM_, int WN_, int NS = NSTAGE,
-          int MINW = 1>
+          int MINW = 1, bool PART = false>
 moe_status launch_dma(const GroupedParams& p, int64_t max_routed_rows, hipStream_t stream) {
-  auto kern = dma_gemm_kernel<BSRC, TL, EPI, BM, BN, WM_, WN_, NS, MINW>;
+  auto kern = dma_gemm_kernel<BSRC, TL, EPI, BM, BN, WM_, WN_, NS, MINW, PART>;
   constexpr int per_cu = MINW * 4 / (WM_ * WN_) > 0 ? MINW * 4 / (WM_ * WN_) : 1;  // workgroups
   constexpr size_t lds = NS * (BM * 2 + BN * (BSRC == B_FP8 ? 1 : 2)) * BKE +
                          (3 * kMaxGroups + 1 + 4) * sizeof(int);
@@ -388,7 +414,7 @@ moe_status launch_dma(const GroupedParams& p, int64_t max_routed_rows, hipStream
   const int ngroups = p.n_routed + (p.t_dense > 0 ? 1 : 0);
   const int64_t m_tiles_ub = (max_routed_rows + BM - 1) / BM + p.n_routed +
                              (p.t_dense > 0 ? (p.t_dense + BM - 1) / BM : 0);
-  const int64_t tiles_ub = m_tiles_ub * nt;
+  const int64_t tiles_ub = m_tiles_ub * nt * (PART ? p.ksplit : 1);
   if (ngroups == 0 || tiles_ub == 0) return MOE_OK;
   int64_t grid = (int64_t)device_info().cus * per_cu;
   if (grid > tiles_ub) grid = tiles_ub;
@@ -434,6 +460,12 @@ moe_status launch_dma_epi(int epi, const GroupedParams& p, int64_t max_routed_ro
 }
 
 }  // namespace
+
+// Split-K fp32 partials for a single dense bf16 GEMM (the E >= 256 router
+// logits): 128x256 tiles, two workgroups per CU.
+moe_status launch_dma_partial(const GroupedParams& p, hipStream_t stream) {
+  return launch_dma<B_SAME, false, EPI_NONE, 128, 256, 1, 4, 3, 2, true>(p, 0, stream);
+}
 
 // bf16 or fp8 weights (row-major or tiled); output columns in whole 256-wide
 // tiles, K in whole 32-element stages (fp8: 128-element scale blocks).

@@ -589,8 +589,35 @@ moe_status run_ffn(const moe_ffn_args* a, const FfnPlan& pl, void* ws, hipStream
 
 }  // namespace
 
+// Split-K slices for the router GEMM on the LDS-DMA kernel (E a multiple of
+// 256: whole 256-wide tiles): enough 128-row x slice work items for two
+// workgroups per CU.
+int dense_logits_ksplit(int64_t T, int d, int E) {
+  if (E % 256 != 0 || d % BKE_DMA != 0) return 1;
+  const int64_t m_tiles = (T + 127) / 128;
+  const int64_t target = 2 * (int64_t)device_info().cus;
+  int ks = 1;
+  while (ks < 16 && m_tiles * ks < target && (d / BKE_DMA) % (2 * ks) == 0) ks *= 2;
+  return ks;
+}
+
 moe_status dense_logits_gemm(const void* x, const void* w_router, float* out, int64_t T, int d,
                              int E, hipStream_t stream) {
+  if (E % 256 == 0 && d % BKE_DMA == 0) {
+    GroupedParams p{};
+    p.a_dense = x;
+    p.bd1 = w_router;
+    p.n_routed = 0;
+    p.t_dense = T;
+    p.K = d;
+    p.N = E;
+    p.ldc = E;
+    p.partial = out;
+    p.ksplit = dense_logits_ksplit(T, d, E);
+    p.prow_total = T;
+    p.max_rows = 0;
+    return launch_dma_partial(p, stream);
+  }
   GroupedParams p{};
   p.a_dense = x;
   p.c_dense = out;

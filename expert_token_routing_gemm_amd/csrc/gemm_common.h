@@ -15,6 +15,7 @@ enum Epi { EPI_NONE = 0, EPI_RELU = 1, EPI_GELU = 2, EPI_SWIGLU = 3 };
 enum BSrc { B_SAME = 0, B_FP8 = 1 };
 
 constexpr int kGemmThreads = 256;
+constexpr int BKE_DMA = 32;  // k elements per stage of the LDS-DMA kernel
 constexpr int kMaxGroups = MOE_MAX_EXPERTS + 1;
 
 struct GroupedParams {
@@ -78,5 +79,6 @@ moe_status launch_stream_gemm2_any(int bsrc, const GroupedParams& p, hipStream_t
 bool dma_gemm_supported(const GroupedParams& p, int bsrc);
 moe_status launch_dma_gemm(int bsrc, int epi, const GroupedParams& p, int64_t max_routed_rows,
                            hipStream_t stream);
+moe_status launch_dma_partial(const GroupedParams& p, hipStream_t stream);
 
 }  // namespace moe

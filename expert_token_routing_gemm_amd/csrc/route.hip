@@ -423,8 +423,9 @@ __device__ __forceinline__ void group_limit(float (&key)[MOE_MAX_EXPERTS / kWave
   }
 }
 
+// logits_in holds ks slices [ks][T][E] of partial sums, added in slice order.
 __global__ void __launch_bounds__(256) topk_kernel(
-    const float* __restrict__ logits_in, const float* __restrict__ b_router,
+    const float* __restrict__ logits_in, int ks, const float* __restrict__ b_router,
     const float* __restrict__ b_select, float* __restrict__ logits_out, int32_t* __restrict__ ids,
     float* __restrict__ weights, int64_t T_tok, int E, int k, int score, int renorm, int ng,
     int tg) {
@@ -444,7 +445,9 @@ __global__ void __launch_bounds__(256) topk_kernel(
       key[i] = -INFINITY;
       sc[i] = 0.f;
       if (e < E) {
-        L[i] = logits_in[t * E + e] + (b_router ? b_router[e] : 0.f);
+        float l = logits_in[t * E + e];
+        for (int z = 1; z < ks; ++z) l += logits_in[(int64_t)z * T_tok * E + t * E + e];
+        L[i] = l + (b_router ? b_router[e] : 0.f);
         if (logits_out) logits_out[t * E + e] = L[i];
         if (score == MOE_SIGMOID) {
           sc[i] = sigmoid_f32_via_f64(L[i]);
@@ -551,9 +554,14 @@ bool mfma_route(const moe_route_args* a) {
 
 using namespace moe;
 
+// Split-K slices of the router logits (1 unless the MFMA path splits K).
+static int route_ksplit(const moe_route_args* a) {
+  return mfma_route(a) ? dense_logits_ksplit(a->T, a->d, a->E) : 1;
+}
+
 extern "C" size_t moe_route_workspace_bytes(const moe_route_args* a) {
   if (!a || a->x == nullptr || small_route_fits(a)) return 0;
-  return align_up((size_t)a->T * a->E * sizeof(float), 256);
+  return align_up((size_t)route_ksplit(a) * a->T * a->E * sizeof(float), 256);
 }
 
 extern "C" moe_status moe_route(const moe_route_args* a, void* ws, size_t ws_bytes,
@@ -584,7 +592,7 @@ extern "C" moe_status moe_route(const moe_route_args* a, void* ws, size_t ws_byt
   if (a->x == nullptr) {
     MOE_CHECK_ARG(a->logits != nullptr, "x == NULL needs input logits");
     MOE_CHECK_ARG(a->b_router == nullptr, "x == NULL: logits are final, b_router must be NULL");
-    topk_kernel<<<grid_for(a->T, 4), tb, 0, stream>>>(a->logits, nullptr, a->b_select, nullptr,
+    topk_kernel<<<grid_for(a->T, 4), tb, 0, stream>>>(a->logits, 1, nullptr, a->b_select, nullptr,
                                                        a->ids, a->weights, a->T, a->E, a->k,
                                                        a->score, a->renorm,
                                                        grouped(a) ? a->n_groups : 0, a->topk_groups);
@@ -635,6 +643,7 @@ extern "C" moe_status moe_route(const moe_route_args* a, void* ws, size_t ws_byt
     return MOE_ERR_WORKSPACE;
   }
   float* raw = static_cast<float*>(ws);
+  const int ks = route_ksplit(a);
   if (mfma_route(a)) {
     const moe_status st = dense_logits_gemm(a->x, a->w_router, raw, a->T, a->d, a->E, stream);
     if (st != MOE_OK) return st;
@@ -650,7 +659,7 @@ extern "C" moe_status moe_route(const moe_route_args* a, void* ws, size_t ws_byt
     }
     MOE_CHECK_LAUNCH();
   }
-  topk_kernel<<<grid_for(a->T, 4), tb, 0, stream>>>(raw, a->b_router, a->b_select, a->logits,
+  topk_kernel<<<grid_for(a->T, 4), tb, 0, stream>>>(raw, ks, a->b_router, a->b_select, a->logits,
                                                      a->ids, a->weights, a->T, a->E, a->k,
                                                      a->score, a->renorm,
                                                      grouped(a) ? a->n_groups : 0, a->topk_groups);
