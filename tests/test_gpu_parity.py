@@ -126,6 +126,9 @@ SMALL = {
     # just above the single-workgroup dispatch limit (T*k > 4096): multi-block path
     "c2-multiblock-dispatch": (2, dict(T=2100, d=256, h=384)),
     "c4-multiblock-dispatch": (4, dict(T=600, d=256, h=256)),
+    # decode-sized batch on the streaming path with skewed routing: experts
+    # of 191 and 72 rows take several 64-row passes over the same weights
+    "c2-decode-skewed": (2, dict(T=256, d=256, h=384)),
 }
 
 
@@ -168,6 +171,16 @@ def test_tiny_edge_shapes():
     full_parity(make_workload(0, T=37, d=128, h=128, E=4, k=4, R=2), label="k=E")
     full_parity(make_workload(1, T=9, d=128, h=128, E=1, k=1), label="E=1")
     full_parity(make_workload(3, T=300, d=128, h=256, E=64, k=1, R=16, cf=0.25), label="heavy drop")
+
+
+def test_zero_capacity_drops_everything():
+    """C = 0: every assignment skips its expert and every token leaves as x."""
+    wl = make_workload(0, T=300, d=128, h=128)
+    layer, g = run_layer(wl, capacity=0)
+    ref = O.dispatch(O.layer(wl, with_ffn=False)["route"]["ids"], wl.E, wl.R, 0)
+    np.testing.assert_array_equal(g["counts"], ref["counts"])
+    assert (g["slot"] == -1).all() and (g["kept"] == 0).all() and int(g["off"][-1]) == 0
+    np.testing.assert_array_equal(g["y"], wl.x)
 
 
 def test_empty_batch():
