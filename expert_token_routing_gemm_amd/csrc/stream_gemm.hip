@@ -10,6 +10,10 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = kGemmThreads;
+#ifndef MOE_SG_WAVES
+#define MOE_SG_WAVES 8  // waves per workgroup of the streaming kernel (share one A staging)
+#endif
+constexpr int kSgThreads = 64 * MOE_SG_WAVES;
 
 // ---------------------------------------------------------------- weight streaming
 // Decode-sized groups (at most a few tens of rows per expert) are bound by
@@ -71,12 +75,12 @@ __device__ __forceinline__ u32x4 load_stream(const unsigned char* ptr) {
 // TL: weights in the 16-row tiled layout (each wave's loads of a chunk are
 // whole contiguous 1 KB pieces; see moe_weight_tile) instead of row-major.
 template <int BSRC, int EPI, int CK, int MINW, bool TL>
-__global__ void __launch_bounds__(kThreads, MINW) stream_gemm_kernel(GroupedParams p) {
+__global__ void __launch_bounds__(kSgThreads, MINW) stream_gemm_kernel(GroupedParams p) {
   constexpr int NMAT = (EPI == EPI_SWIGLU) ? 2 : 1;
   constexpr int V = CK / 32;                 // 16-byte bf16 pieces per lane per matrix
   constexpr int RS = CK * 2 + 16;            // LDS row stride (bytes)
   constexpr int MROWS = 64;                  // rows per pass
-  constexpr int A_PIECES = MROWS * CK * 2 / 16 / kThreads;  // 16-byte A pieces per thread
+  constexpr int A_PIECES = MROWS * CK * 2 / 16 / kSgThreads;  // 16-byte A pieces per thread
   constexpr int QB = CK / 4;                 // K elements per lane group per chunk
   constexpr bool SKIP = (EPI == EPI_SWIGLU) ? MOE_SG_SKIP : MOE_DN_SKIP;
   constexpr bool IL = MOE_SG_IL || TL;
@@ -121,7 +125,7 @@ __global__ void __launch_bounds__(kThreads, MINW) stream_gemm_kernel(GroupedPara
       Sm[1] = dense ? p.sd3 : (p.s3 ? p.s3 + (int64_t)g * p.ns * p.ks : nullptr);
     }
   }
-  const int ocol0 = blockIdx.x * 64 + wave * 16;  // first output column of this wave
+  const int ocol0 = blockIdx.x * (16 * MOE_SG_WAVES) + wave * 16;  // first output column of this wave
   const int brow = ocol0 + (lane & 15);            // the weight row this lane streams
   const int NC = p.K / CK / p.ksplit;       // chunks of this block's K slice
   const int cb = blockIdx.z * NC;           // first chunk of the slice
@@ -174,7 +178,7 @@ __global__ void __launch_bounds__(kThreads, MINW) stream_gemm_kernel(GroupedPara
     const unsigned char* a_row[A_PIECES];
 #pragma unroll
     for (int i = 0; i < A_PIECES; ++i) {
-      const int c_ = tid + i * kThreads;
+      const int c_ = tid + i * kSgThreads;
       const int rr_ = min(m0 + c_ / PR, rows - 1);
       a_row[i] = reinterpret_cast<const unsigned char*>(A + (int64_t)rr_ * p.K) + (c_ % PR) * 16;
     }
@@ -183,7 +187,7 @@ __global__ void __launch_bounds__(kThreads, MINW) stream_gemm_kernel(GroupedPara
       areg[ABUF_][i] = *reinterpret_cast<const u32x4*>(a_row[i] + (int64_t)(C_) * CK * 2);
 #define MOE_STREAM_STORE_A(ABUF_, BUF_)                                                    \
     _Pragma("unroll") for (int i = 0; i < A_PIECES; ++i) {                                 \
-      const int c_ = tid + i * kThreads;                                                   \
+      const int c_ = tid + i * kSgThreads;                                                 \
       *reinterpret_cast<u32x4*>(lds_a + (BUF_) * MROWS * RS + (c_ / PR) * RS +             \
                                 (c_ % PR) * 16) = areg[ABUF_][i];                          \
     }
@@ -385,8 +389,8 @@ moe_status launch_stream(const GroupedParams& p, hipStream_t stream) {
   const int ngroups = p.n_routed + (p.t_dense > 0 ? 1 : 0);
   const int out_cols = (EPI == EPI_SWIGLU) ? p.N / 2 : p.N;
   if (ngroups == 0) return MOE_OK;
-  dim3 grid(out_cols / 64, ngroups, p.ksplit);
-  kern<<<grid, kThreads, lds, stream>>>(p);
+  dim3 grid(out_cols / (16 * MOE_SG_WAVES), ngroups, p.ksplit);
+  kern<<<grid, kSgThreads, lds, stream>>>(p);
   MOE_CHECK_LAUNCH();
   if (p.ksplit > 1) {
     const int64_t n4 = p.prow_total * (out_cols / 4);
@@ -409,7 +413,7 @@ moe_status launch_stream(const GroupedParams& p, hipStream_t stream) {
 #define MOE_KSPLIT_WAVES_PER_CU 12
 #endif
 int stream_ksplit(int ngroups, int out_cols, int K, int CK) {
-  const int64_t waves = (int64_t)ngroups * (out_cols / 64) * 4;
+  const int64_t waves = (int64_t)ngroups * (out_cols / 16);
   const int64_t target = (int64_t)device_info().cus * MOE_KSPLIT_WAVES_PER_CU;
   int ks = 1;
   while (ks < MOE_MAX_KSPLIT && waves * ks < target && (K / CK) % (2 * ks) == 0) ks *= 2;
