@@ -164,33 +164,52 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
   const int KS = PART ? p.ksplit : 1;
   const int KT = p.K / BKE / KS;  // stages of one K slice
 
-  for (int work = first; work < total * KS; work += G) {
-    const int z = work / total;  // K slice (consecutive work items share it)
-    const int tile = work - z * total;
-    const int kbase = z * KT;
+  // Per-tile state.  The next tile's setup and first stages are issued
+  // before the current tile's epilogue, so its loads overlap the epilogue's
+  // activation math and stores.
+  struct Ctx {
+    int z, kbase, g, rows, m0, n_t;
+    bool dense;
+    bf16_t* C;
+    const unsigned char* src[LPW];  // stage-0 global address of each DMA instruction
+    int kstep[LPW];                 // its bytes per stage
+    const float* sp[QN];            // fp8 scale rows of the B subtiles
+  };
+  // DMA instruction i of this wave fills 1 KB block b = wave + NW*i of the
+  // stage (A blocks first, then B blocks); LDS position l*16 <- lane l.
+  const int dr = lane >> 2;                 // row-major 16-bit: row
+  const int dchunk = (lane & 3) ^ swz(dr);  //   and logical chunk
+  auto setup = [&](int work, Ctx& c) {
+    c.z = work / total;  // K slice (consecutive work items share it)
+    const int tile = work - c.z * total;
+    c.kbase = c.z * KT;
     int lo = 0, hi = ngroups - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (s_tstart[mid] <= tile) lo = mid; else hi = mid - 1;
     }
+    c.g = lo;
     const int g = lo;
     const int local = tile - s_tstart[g];
-    const int rows = s_rows[g];
+    c.rows = s_rows[g];
+    const int rows = c.rows;
     const int mt = (rows + BM - 1) / BM;
     const int strip = local / (kGM * nt);
     const int rem = local - strip * kGM * nt;
     const int gm = min(kGM, mt - strip * kGM);
     const int m_t = strip * kGM + rem % gm;
     const int n_t = rem / gm;
+    c.n_t = n_t;
     const bool dense = g >= p.n_routed;
+    c.dense = dense;
     const int m0 = m_t * BM;
+    c.m0 = m0;
 
     const unsigned char *A, *B1, *B3;
     const float *S1 = nullptr, *S3 = nullptr;
-    bf16_t* C;
     if (!dense) {
       A = reinterpret_cast<const unsigned char*>(p.a_routed) + (int64_t)(s_r0[g] - a_sub) * a_stride;
-      C = reinterpret_cast<bf16_t*>(p.c_routed) + (int64_t)(s_r0[g] - c_sub) * p.ldc;
+      c.C = reinterpret_cast<bf16_t*>(p.c_routed) + (int64_t)(s_r0[g] - c_sub) * p.ldc;
       B1 = reinterpret_cast<const unsigned char*>(p.b1) + (int64_t)g * b_mat;
       B3 = p.b3 ? reinterpret_cast<const unsigned char*>(p.b3) + (int64_t)g * b_mat : B1;
       if (F8) {
@@ -199,7 +218,7 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
       }
     } else {
       A = reinterpret_cast<const unsigned char*>(p.a_dense);
-      C = reinterpret_cast<bf16_t*>(p.c_dense);
+      c.C = reinterpret_cast<bf16_t*>(p.c_dense);
       B1 = reinterpret_cast<const unsigned char*>(p.bd1);
       B3 = p.bd3 ? reinterpret_cast<const unsigned char*>(p.bd3) : B1;
       if (F8) {
@@ -225,18 +244,14 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
 
     // DMA instruction i of this wave fills 1 KB block b = wave + NW*i of the
     // stage (A blocks first, then B blocks); LDS position l*16 <- lane l.
-    // src[i] is the stage-0 global address, kstep[i] the bytes per stage.
-    const int dr = lane >> 2;                      // row-major 16-bit: row
-    const int dchunk = (lane & 3) ^ swz(dr);       //   and logical chunk
-    const unsigned char* src[LPW];
-    int kstep[LPW];
+    // c.src[i] is the stage-0 global address, c.kstep[i] the bytes per stage.
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int b = wave + NW * i;
       if (b < A_BLOCKS) {
         const int ar = min(m0 + 16 * b + dr, rows - 1);
-        src[i] = A + (int64_t)ar * a_stride + dchunk * 16;
-        kstep[i] = BKE * 2;
+        c.src[i] = A + (int64_t)ar * a_stride + dchunk * 16;
+        c.kstep[i] = BKE * 2;
       } else {
         int r_in;  // row inside the block
         if (F8) r_in = TL ? 16 * (lane >> 5) + (lane & 15) : (lane >> 1);
@@ -248,59 +263,69 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
         if (TL) {
           // 16-row tile: 1 KB pieces of 64 bytes per row, in lane order
           const int64_t tile_base = (int64_t)(brow >> 4) * 16 * b_stride;
-          src[i] = bm + tile_base + (F8 ? (lane & 31) : lane) * 16;
-          kstep[i] = F8 ? 512 : 1024;  // fp8: half kt%2 of piece kt/2
+          c.src[i] = bm + tile_base + (F8 ? (lane & 31) : lane) * 16;
+          c.kstep[i] = F8 ? 512 : 1024;  // fp8: half kt%2 of piece kt/2
         } else {
-          src[i] = bm + (int64_t)brow * b_stride + (F8 ? (lane & 1) : dchunk) * 16;
-          kstep[i] = BKE * (F8 ? 1 : 2);
+          c.src[i] = bm + (int64_t)brow * b_stride + (F8 ? (lane & 1) : dchunk) * 16;
+          c.kstep[i] = BKE * (F8 ? 1 : 2);
         }
       }
     }
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) src[i] += (int64_t)kbase * kstep[i];
-    auto issue = [&](int kt) {
-      unsigned char* st = ring + (kt % NS) * STAGE_BYTES;
-#pragma unroll
-      for (int i = 0; i < LPW; ++i) {
-        const int b = wave + NW * i;
-        __builtin_amdgcn_global_load_lds(MOE_GPTR(src[i] + (int64_t)kt * kstep[i]),
-                                         MOE_LPTR(st + b * 1024), 16, 0, 0);
-      }
-    };
+    for (int i = 0; i < LPW; ++i) c.src[i] += (int64_t)c.kbase * c.kstep[i];
     // fp8 scales: one per B subtile and 128-k block (the subtile's 32
     // weight rows lie in one 128-row block)
-    const float* sp[QN];
     if constexpr (F8) {
 #pragma unroll
       for (int j = 0; j < QN; ++j) {
         const unsigned char* bm;
         const float* sm;
         const int brow = b_row(wn * WTN + j * 32, bm, sm);
-        sp[j] = sm + (int64_t)(brow >> 7) * p.ks;
+        c.sp[j] = sm + (int64_t)(brow >> 7) * p.ks;
       }
     }
 
+  };
+  auto issue = [&](const Ctx& c, int kt) {
+    unsigned char* st = ring + (kt % NS) * STAGE_BYTES;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int b = wave + NW * i;
+      __builtin_amdgcn_global_load_lds(MOE_GPTR(c.src[i] + (int64_t)kt * c.kstep[i]),
+                                       MOE_LPTR(st + b * 1024), 16, 0, 0);
+    }
+  };
+
+  const int W = total * KS;
+  Ctx cur;
+  if (first < W) {
+    setup(first, cur);
+    // every wave has finished reading the tile table's neighbours; ring free
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+      if (s < KT) issue(cur, s);
+  }
+  for (int work = first; work < W; work += G) {
     f32x16 acc[QM][QN];
 #pragma unroll
     for (int i = 0; i < QM; ++i)
 #pragma unroll
       for (int j = 0; j < QN; ++j) acc[i][j] = f32x16{};
 
-    // every wave has finished reading the ring of the previous tile
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-#pragma unroll
-    for (int s = 0; s < NS - 1; ++s)
-      if (s < KT) issue(s);
+    const int rows = cur.rows, m0 = cur.m0, n_t = cur.n_t, z = cur.z, kbase = cur.kbase, g = cur.g;
+    const bool dense = cur.dense;
+    bf16_t* const C = cur.C;
 
     const int h = lane >> 5;  // k half of this lane: [16h, 16h + 16) of a stage
     for (int kt = 0; kt < KT; ++kt) {
       float sc[QN];
       if constexpr (F8) {
 #pragma unroll
-        for (int j = 0; j < QN; ++j) sc[j] = sp[j][(kbase + kt) >> 2];
+        for (int j = 0; j < QN; ++j) sc[j] = cur.sp[j][(kbase + kt) >> 2];
       }
       wait_stage_and_barrier<LPW>(min(NS - 2, KT - 1 - kt));
-      if (kt + NS - 1 < KT) issue(kt + NS - 1);
+      if (kt + NS - 1 < KT) issue(cur, kt + NS - 1);
       const unsigned char* st = ring + (kt % NS) * STAGE_BYTES;
       u32x4 bq[QN][2];  // B fragments of both k-steps
 #pragma unroll
@@ -349,6 +374,16 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
       }
     }
 
+    // every wave has finished reading the ring: start the next tile's loads
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const bool more = work + G < W;
+    Ctx nxt;
+    if (more) {
+      setup(work + G, nxt);
+#pragma unroll
+      for (int s = 0; s < NS - 1; ++s)
+        if (s < KT) issue(nxt, s);
+    }
     // epilogue: value v of a lane is row 8*(v/4) + 4*(lane/32) + v%4,
     // column lane%32 of its 32x32 subtile
     if constexpr (PART) {
@@ -365,33 +400,36 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
           for (int j = 0; j < QN; ++j) prow[n_t * BN + wn * WTN + j * 32 + (lane & 31)] = acc[i][j][v];
         }
       }
-      continue;
-    }
+    } else {
 #pragma unroll
-    for (int i = 0; i < QM; ++i) {
+      for (int i = 0; i < QM; ++i) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm * WTM + i * 32 + 8 * (v / 4) + 4 * (lane >> 5) + (v % 4);
-        if (row >= rows) continue;
-        bf16_t* crow = C + (int64_t)row * p.ldc;
-        if (EPI == EPI_SWIGLU) {
+        for (int v = 0; v < 16; ++v) {
+          const int row = m0 + wm * WTM + i * 32 + 8 * (v / 4) + 4 * (lane >> 5) + (v % 4);
+          if (row >= rows) continue;
+          bf16_t* crow = C + (int64_t)row * p.ldc;
+          if (EPI == EPI_SWIGLU) {
 #pragma unroll
-          for (int j = 0; j < QN / 2; ++j) {
-            const int col = n_t * (BN / 2) + wn * (WTN / 2) + j * 32 + (lane & 31);
-            crow[col] = (bf16_t)f32_to_bf16(act_silu(acc[i][j][v]) * acc[i][j + QN / 2][v]);
-          }
-        } else {
+            for (int j = 0; j < QN / 2; ++j) {
+              const int col = n_t * (BN / 2) + wn * (WTN / 2) + j * 32 + (lane & 31);
+              crow[col] = (bf16_t)f32_to_bf16(act_silu(acc[i][j][v]) * acc[i][j + QN / 2][v]);
+            }
+          } else {
 #pragma unroll
-          for (int j = 0; j < QN; ++j) {
-            const int col = n_t * BN + wn * WTN + j * 32 + (lane & 31);
-            float x = acc[i][j][v];
-            if (EPI == EPI_RELU) x = fmaxf(x, 0.f);
-            if (EPI == EPI_GELU) x = act_gelu(x);
-            crow[col] = (bf16_t)f32_to_bf16(x);
+            for (int j = 0; j < QN; ++j) {
+              const int col = n_t * BN + wn * WTN + j * 32 + (lane & 31);
+              float x = acc[i][j][v];
+              if (EPI == EPI_RELU) x = fmaxf(x, 0.f);
+              if (EPI == EPI_GELU) x = act_gelu(x);
+              crow[col] = (bf16_t)f32_to_bf16(x);
+            }
           }
         }
       }
     }
+    // the next tile's first stages (and these stores) have landed
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (more) cur = nxt;
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
