@@ -259,6 +259,29 @@ def bias_update(b_select32: np.ndarray, counts: np.ndarray, T: int, k: int, gamm
     return (np.asarray(b_select32, F32) - np.float32(gamma) * sgn).astype(F32)
 
 
+def aux_balance_loss(L64: np.ndarray, counts: np.ndarray, k: int, score: str, alpha: float):
+    """Auxiliary balancing loss value of one step (forward only).  The pages
+    say only that an extra loss term rewards the router for spreading tokens
+    evenly (Ultralytics, "Load Balancing and Capacity", auxiliary-loss bullet;
+    ai360xpert, "Load Balancing and Dropped Tokens", auxiliary-loss bullet).
+    Reading taken, the Switch-Transformer form:
+        loss = alpha * E * sum_e f_e * P_e,
+    f_e = counts_e / (T*k) the fraction of the step's assignments (before
+    capacity) routed to e, P_e the mean over tokens of the router's
+    probability for e: softmax over all E, or for sigmoid scoring the
+    sigmoids normalised per token.  Returns (P [E], loss)."""
+    L64 = np.asarray(L64, F64)
+    T, E = L64.shape
+    if score == "softmax":
+        p = softmax(L64)
+    else:
+        sg = sigmoid(L64)
+        p = sg / sg.sum(axis=1, keepdims=True)
+    P = p.mean(axis=0) if T > 0 else np.zeros(E)
+    f = np.asarray(counts, F64) / (T * k) if T > 0 else np.zeros(E)
+    return P, float(alpha) * E * float(np.dot(f, P))
+
+
 # --------------------------------------------------------------------------
 # Dispatch
 # --------------------------------------------------------------------------

@@ -534,3 +534,49 @@ def test_bias_update_balances_skewed_routing():
         b = O.bias_update(b, counts, T, k, gamma=0.01)
     last = counts.max() / (T * k / E)
     assert first > 2.0 and last < 0.6 * first
+
+
+# ---------------------------------------------------------------- auxiliary loss
+# Pins of the auxiliary balancing loss (closed forms and invariants, not the
+# formula retyped): perfectly even routing with uniform probabilities gives
+# exactly alpha; everything on one expert with probability -> 1 gives alpha*E;
+# the mean probabilities sum to 1; relabelling experts permutes P and leaves
+# the loss unchanged; the loss is linear in alpha.
+
+
+def test_aux_loss_even_routing_is_alpha():
+    T, E, k = 64, 8, 2
+    L = np.zeros((T, E))
+    counts = np.full(E, T * k // E)
+    for score in ("softmax", "sigmoid"):
+        P, loss = O.aux_balance_loss(L, counts, k, score, 0.01)
+        np.testing.assert_allclose(P, 1.0 / E, rtol=0, atol=1e-15)
+        assert abs(loss - 0.01) < 1e-15
+
+
+def test_aux_loss_collapse_is_alpha_times_E():
+    T, E, k = 32, 16, 1
+    L = np.full((T, E), -60.0)
+    L[:, 3] = 60.0
+    counts = np.zeros(E, np.int64)
+    counts[3] = T
+    P, loss = O.aux_balance_loss(L, counts, k, "softmax", 0.5)
+    assert abs(loss - 0.5 * E) < 1e-9
+    assert abs(P[3] - 1.0) < 1e-12
+
+
+def test_aux_loss_invariants():
+    rng = np.random.default_rng(4)
+    T, E, k = 50, 12, 3
+    L = rng.standard_normal((T, E)) * 2
+    ids = O.topk_select(L.astype(np.float32), k)
+    counts = np.bincount(ids.ravel(), minlength=E)
+    perm = rng.permutation(E)
+    for score in ("softmax", "sigmoid"):
+        P, loss = O.aux_balance_loss(L, counts, k, score, 0.1)
+        assert abs(P.sum() - 1.0) < 1e-12
+        P2, loss2 = O.aux_balance_loss(L[:, perm], counts[perm], k, score, 0.1)
+        np.testing.assert_allclose(P2, P[perm], rtol=1e-13)
+        assert abs(loss2 - loss) < 1e-13
+        _, loss3 = O.aux_balance_loss(L, counts, k, score, 0.3)
+        assert abs(loss3 - 3 * loss) < 1e-13
