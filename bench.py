@@ -133,6 +133,48 @@ def cpu_baseline(wl, budget_s: float = 10.0, max_reps: int = 8):
                       f"{dt:.1f} s in total (input generation excluded)"}
 
 
+def extras(M, wl, layer, hip, args):
+    """Measured outside the timed region: the auxiliary-loss kernel on
+    logits of the workload's shape, and (workloads with a selection bias) a
+    route -> dispatch -> bias-update loop on the workload's own router."""
+    import numpy as np
+    import torch
+    ev = Events(hip, 2)
+    logits = torch.randn((wl.T, wl.E), device="cuda:0")
+    M.moe_aux_loss(logits, layer.counts, wl.k, M.SCORE[wl.score], 0.01)
+    torch.cuda.synchronize()
+    reps = 20
+    st = torch.cuda.current_stream().cuda_stream
+    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventRecord(ev.ev[0], st)
+    for _ in range(reps):
+        M.moe_aux_loss(logits, layer.counts, wl.k, M.SCORE[wl.score], 0.01)
+    hip.hipEventRecord(ev.ev[1], st)
+    torch.cuda.synchronize()
+    out = {"aux_loss_us": ev.ms(0, 1) * 1e3 / reps}
+    ev.close()
+    if wl.b_select is None or args.balance_steps <= 0:
+        out["balance"] = None
+        return out
+    mean = wl.T * wl.k / wl.E
+    loads = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.balance_steps):
+        layer.route()
+        layer.dispatch()
+        loads.append(layer.counts.max())
+        layer.update_bias(args.balance_gamma)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    loads = [int(x.item()) / mean for x in loads]
+    out["balance"] = {"steps": args.balance_steps, "gamma": args.balance_gamma,
+                      "max_over_mean_load": [round(loads[0], 3), round(min(loads), 3), round(loads[-1], 3)],
+                      "ms_per_step": dt * 1e3 / args.balance_steps,
+                      "step": "route + dispatch + bias update (wall clock, host loop)"}
+    return out
+
+
 def copy_probe(mib: int, steps: int):
     """A plain copy of known size (and a read-only reduction) on the device:
     the reference for scaling the rocprofv3 byte counters and the measured
@@ -169,6 +211,10 @@ def main():
                     help="expert weight layout (default: tiled, re-laid out once at load time, "
                          "wherever the kernels take it, i.e. bf16 activations; row-major for "
                          "the fp32 workload)")
+    ap.add_argument("--balance-steps", type=int, default=30,
+                    help="after the timed region: route -> dispatch -> bias update steps on "
+                         "workloads with a selection bias (reports max/mean expert load)")
+    ap.add_argument("--balance-gamma", type=float, default=0.01)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead of the layer: time a plain device copy of MIB MiB (HBM "
                          "calibration for the traffic counters) and a full read (sum)")
@@ -277,6 +323,7 @@ def main():
         "gpu_ms_per_step": gpu_ms / K,
         "roofline": roof,
     }
+    out["extras"] = extras(M, wl, layer, hip, args)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl)

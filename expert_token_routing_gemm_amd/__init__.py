@@ -108,6 +108,21 @@ def moe_bias_update(counts: torch.Tensor, b_select: torch.Tensor, T: int, k: int
                                  float(gamma), _stream(stream)), "moe_bias_update")
 
 
+def moe_aux_loss(logits: torch.Tensor, counts: torch.Tensor, k: int, score: int, alpha: float,
+                 stream=None):
+    """Auxiliary balancing loss of one step: (prob_mean [E], loss [1]) device
+    tensors from the router's fp32 logits [T, E] and the raw counts [E]."""
+    T, E = logits.shape
+    ws = torch.empty((max(int(lib().moe_aux_loss_workspace_bytes(T, E)), 256),), dtype=torch.uint8,
+                     device=logits.device)
+    pm = torch.empty((E,), dtype=torch.float32, device=logits.device)
+    loss = torch.empty((1,), dtype=torch.float32, device=logits.device)
+    _check(lib().moe_aux_loss(_p(logits), _p(counts), int(T), int(E), int(k), int(score),
+                              float(alpha), _p(pm), _p(loss), _p(ws), ws.numel(), _stream(stream)),
+           "moe_aux_loss")
+    return pm, loss
+
+
 def moe_weight_tile(w: torch.Tensor, n_mats: int, rows: int, stream=None) -> torch.Tensor:
     """A new device tensor holding the n_mats [rows, *] matrices of ``w``
     (contiguous) in the 16-row tiled layout of the streaming kernels."""
@@ -256,6 +271,13 @@ class MoELayer:
         self.workspace = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
 
     # single stages (each one C call)
+    def aux_loss(self, alpha: float, stream=None):
+        """Auxiliary balancing loss of the last route + dispatch (needs the
+        logits kept): (prob_mean [E], loss [1]) device tensors."""
+        if self.logits is None:
+            raise ValueError("the layer does not keep its logits")
+        return moe_aux_loss(self.logits, self.counts, self.k, SCORE[self.wl.score], alpha, stream)
+
     def update_bias(self, gamma: float, stream=None) -> None:
         """One bias-balancing step from the last dispatch's raw counts."""
         if self.b_select is None:

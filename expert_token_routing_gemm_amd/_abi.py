@@ -70,6 +70,9 @@ PROTOTYPES = {
     "moe_capacity": (C.c_int32, [C.c_int64, C.c_int32, C.c_int32, C.c_double]),
     "moe_send_rows_max": (C.c_int64, [C.c_int64, C.c_int32, C.c_int32, C.c_int32]),
     "moe_bias_update": (C.c_int, [vp, vp, C.c_int32, C.c_int64, C.c_int32, C.c_float, vp]),
+    "moe_aux_loss_workspace_bytes": (C.c_size_t, [C.c_int64, C.c_int32]),
+    "moe_aux_loss": (C.c_int, [vp, vp, C.c_int64, C.c_int32, C.c_int32, C.c_int32, C.c_float, vp,
+                               vp, vp, C.c_size_t, vp]),
     "moe_dispatch_workspace_bytes": (C.c_size_t, [C.POINTER(DispatchArgs)]),
     "moe_dispatch": (C.c_int, [C.POINTER(DispatchArgs), vp, C.c_size_t, vp]),
     "moe_ffn_workspace_bytes": (C.c_size_t, [C.POINTER(FfnArgs)]),

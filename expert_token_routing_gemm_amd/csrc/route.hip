@@ -535,15 +535,6 @@ bool small_route_fits(const moe_route_args* a) {
   return !grouped(a) && a->E <= 8 && (size_t)a->E * a->d * es <= 64 * 1024;
 }
 
-__global__ void __launch_bounds__(256) bias_update_kernel(const int32_t* __restrict__ counts,
-                                                         float* __restrict__ b, int E, int64_t tk,
-                                                         float gamma) {
-  const int e = threadIdx.x;
-  if (e >= E) return;
-  const int64_t c = (int64_t)counts[e] * E;
-  const float s = c > tk ? 1.f : (c < tk ? -1.f : 0.f);
-  b[e] = b[e] - gamma * s;
-}
 
 bool mfma_route(const moe_route_args* a) {
   return a->act_dtype == MOE_BF16 && a->E % 64 == 0 && a->d % 128 == 0 && !small_route_fits(a);
@@ -663,17 +654,6 @@ extern "C" moe_status moe_route(const moe_route_args* a, void* ws, size_t ws_byt
                                                      a->ids, a->weights, a->T, a->E, a->k,
                                                      a->score, a->renorm,
                                                      grouped(a) ? a->n_groups : 0, a->topk_groups);
-  MOE_CHECK_LAUNCH();
-  return MOE_OK;
-}
-
-extern "C" moe_status moe_bias_update(const int32_t* counts, float* b_select, int32_t E, int64_t T,
-                                      int32_t k, float gamma, hipStream_t stream) {
-  clear_error();
-  MOE_CHECK_ARG(E >= 1 && E <= MOE_MAX_EXPERTS, "E out of range [1, 256]");
-  MOE_CHECK_ARG(T >= 0 && k >= 1, "bad T or k");
-  MOE_CHECK_ARG(counts && b_select, "null pointer");
-  bias_update_kernel<<<1, 256, 0, stream>>>(counts, b_select, E, T * (int64_t)k, gamma);
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }

@@ -166,6 +166,24 @@ moe_status moe_dispatch(const moe_dispatch_args* a, void* workspace, size_t ws_b
 moe_status moe_bias_update(const int32_t* counts, float* b_select, int32_t E, int64_t T,
                            int32_t k, float gamma, hipStream_t stream);
 
+/* Auxiliary balancing loss value of one step, forward only (Ultralytics,
+ * "Load Balancing and Capacity", auxiliary-loss bullet; ai360xpert, "Load
+ * Balancing and Dropped Tokens": an extra loss term rewards the router for
+ * spreading tokens evenly).  The pages give no formula; the
+ * Switch-Transformer form is computed:
+ *   P_e  = mean over the T tokens of the router probability of expert e
+ *          (softmax of the logits, or for MOE_SIGMOID the sigmoids
+ *          normalised per token),
+ *   loss = alpha * E * sum_e counts[e] / (T * k) * P_e.
+ * logits [T, E] fp32 are the router's final logits (moe_route's output),
+ * counts [E] the raw per-expert assignment counts (moe_dispatch's output).
+ * Writes prob_mean [E] and loss [1] (device).  Sums run in a fixed order
+ * (deterministic).  T = 0 gives zeros.  Workspace: moe_aux_loss_workspace_bytes. */
+size_t moe_aux_loss_workspace_bytes(int64_t T, int32_t E);
+moe_status moe_aux_loss(const float* logits, const int32_t* counts, int64_t T, int32_t E,
+                        int32_t k, int32_t score, float alpha, float* prob_mean, float* loss,
+                        void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------- expert FFN
  * Local expert compute (Ultralytics, "How Tokens Move Between GPUs", step 3;
  * experts are independent).  For each executed expert e in [e_begin, e_end)

@@ -170,3 +170,36 @@ def test_bias_balancing_loop_bit_exact():
         imb.append(counts.max() / (wl.T * wl.k / wl.E))
     _say(f"[bias] max/mean load {imb[0]:.2f} -> {imb[-1]:.2f}")
     assert imb[-1] < 0.25 * imb[0]
+
+
+# ------------------------------------------------------------------ auxiliary loss
+
+
+@pytest.mark.parametrize("cfg,over", [(4, dict(T=512, d=256, h=256)), (2, dict(T=2048, d=256, h=256)),
+                                      (3, dict(T=37, d=256, h=256)), (4, dict(T=8192, d=256, h=256))])
+def test_aux_loss_matches_oracle(cfg, over):
+    """The loss value and the mean probabilities from the GPU's own fp32
+    logits and counts, against the fp64 oracle on the same inputs."""
+    from expert_token_routing_gemm_amd import MoELayer, to_host
+    wl = make_workload(cfg, **over)
+    _say(f"[aux] cfg{cfg} T={wl.T} E={wl.E} score={wl.score}")
+    layer = MoELayer(wl)
+    layer.route()
+    layer.dispatch()
+    pm, loss = layer.aux_loss(0.01)
+    L32 = to_host(layer.logits)
+    counts = to_host(layer.counts)
+    P, ref = O.aux_balance_loss(L32.astype(np.float64), counts, wl.k, wl.score, 0.01)
+    np.testing.assert_allclose(to_host(pm), P, rtol=2e-5, atol=1e-8)
+    np.testing.assert_allclose(to_host(loss)[0], ref, rtol=2e-5)
+    pm2, loss2 = layer.aux_loss(0.01)  # deterministic
+    np.testing.assert_array_equal(to_host(pm2), to_host(pm))
+    np.testing.assert_array_equal(to_host(loss2), to_host(loss))
+
+
+def test_aux_loss_empty_batch():
+    from expert_token_routing_gemm_amd import moe_aux_loss, to_host
+    logits = torch.empty((0, 8), dtype=torch.float32, device="cuda")
+    counts = torch.zeros((8,), dtype=torch.int32, device="cuda")
+    pm, loss = moe_aux_loss(logits, counts, 2, 0, 0.01)
+    assert (to_host(pm) == 0).all() and to_host(loss)[0] == 0
