@@ -54,16 +54,6 @@ constexpr int kSgThreads = 64 * MOE_SG_WAVES;
 #ifndef MOE_SG_NT
 #define MOE_SG_NT 1
 #endif
-// Lane-group K layout inside a chunk.  0: group q owns one contiguous run of
-// CK/4 elements.  1: interleaved, each 16-byte load of the wave covers 64
-// contiguous bytes of each of its 16 weight rows.
-#ifndef MOE_SG_IL
-#define MOE_SG_IL 1
-#endif
-// 1: A rows of a chunk are fetched one chunk ahead, before its weights.
-#ifndef MOE_SG_AHEAD
-#define MOE_SG_AHEAD 0
-#endif
 
 template <bool TL>
 __device__ __forceinline__ u32x4 load_stream(const unsigned char* ptr) {
@@ -81,9 +71,7 @@ __global__ void __launch_bounds__(kSgThreads, MINW) stream_gemm_kernel(GroupedPa
   constexpr int RS = CK * 2 + 16;            // LDS row stride (bytes)
   constexpr int MROWS = 64;                  // rows per pass
   constexpr int A_PIECES = MROWS * CK * 2 / 16 / kSgThreads;  // 16-byte A pieces per thread
-  constexpr int QB = CK / 4;                 // K elements per lane group per chunk
   constexpr bool SKIP = (EPI == EPI_SWIGLU) ? MOE_SG_SKIP : MOE_DN_SKIP;
-  constexpr bool IL = MOE_SG_IL || TL;
   static_assert(A_PIECES >= 1, "chunk too small");
   static_assert(BSRC != B_FP8 || CK <= 128, "one fp8 scale block per chunk");
   static_assert(BSRC != B_FP8 || CK >= 64, "fp8 chunks hold whole 16-byte loads per lane");
@@ -130,18 +118,20 @@ __global__ void __launch_bounds__(kSgThreads, MINW) stream_gemm_kernel(GroupedPa
   const int NC = p.K / CK / p.ksplit;       // chunks of this block's K slice
   const int cb = blockIdx.z * NC;           // first chunk of the slice
 
-  // per-lane byte pointers into the weight rows (lane group q owns QB elements)
+  // per-lane byte pointers into the weight rows
   const unsigned char* bptr[NMAT];
 #pragma unroll
   for (int m = 0; m < NMAT; ++m)
     bptr[m] = TL ? Bm[m] + (int64_t)ocol0 * p.K * bes + lane * 16
-                 : Bm[m] + (int64_t)brow * p.K * bes + (IL ? q * 16 : q * QB * bes);
-  constexpr int VSTEP = TL ? 1024 : (IL ? 64 : 16);  // bytes between a lane's loads in a chunk
+                 : Bm[m] + (int64_t)brow * p.K * bes + q * 16;
+  // bytes between a lane's loads in a chunk: each 16-byte load of the wave
+  // covers 64 contiguous bytes of each of its 16 weight rows (row-major) or
+  // one whole 1 KB tile piece (tiled)
+  constexpr int VSTEP = TL ? 1024 : 64;
   const int64_t cstride = TL ? (int64_t)CK * bes * 16 : (int64_t)CK * bes;  // per chunk
   // K offset (elements, inside the chunk) of the 8 values lane group q feeds
   // to MFMA step s; the A fragments use the same map
   auto koff = [&](int s_) {
-    if constexpr (!IL) return q * QB + s_ * 8;
     if constexpr (BSRC == B_FP8) return (s_ >> 1) * 64 + q * 16 + (s_ & 1) * 8;
     return s_ * 32 + q * 8;
   };
@@ -174,7 +164,7 @@ __global__ void __launch_bounds__(kSgThreads, MINW) stream_gemm_kernel(GroupedPa
     // compiler can count outstanding loads exactly and the weight prefetch
     // issued before the A store stays in flight.
     constexpr int PR = CK * 2 / 16;
-    u32x4 areg[2][A_PIECES];
+    u32x4 areg[A_PIECES];
     const unsigned char* a_row[A_PIECES];
 #pragma unroll
     for (int i = 0; i < A_PIECES; ++i) {
@@ -182,14 +172,14 @@ __global__ void __launch_bounds__(kSgThreads, MINW) stream_gemm_kernel(GroupedPa
       const int rr_ = min(m0 + c_ / PR, rows - 1);
       a_row[i] = reinterpret_cast<const unsigned char*>(A + (int64_t)rr_ * p.K) + (c_ % PR) * 16;
     }
-#define MOE_STREAM_LOAD_A(ABUF_, C_)                                                       \
+#define MOE_STREAM_LOAD_A(C_)                                                              \
     _Pragma("unroll") for (int i = 0; i < A_PIECES; ++i)                                   \
-      areg[ABUF_][i] = *reinterpret_cast<const u32x4*>(a_row[i] + (int64_t)(C_) * CK * 2);
-#define MOE_STREAM_STORE_A(ABUF_, BUF_)                                                    \
+      areg[i] = *reinterpret_cast<const u32x4*>(a_row[i] + (int64_t)(C_) * CK * 2);
+#define MOE_STREAM_STORE_A(BUF_)                                                           \
     _Pragma("unroll") for (int i = 0; i < A_PIECES; ++i) {                                 \
       const int c_ = tid + i * kSgThreads;                                                 \
       *reinterpret_cast<u32x4*>(lds_a + (BUF_) * MROWS * RS + (c_ / PR) * RS +             \
-                                (c_ % PR) * 16) = areg[ABUF_][i];                          \
+                                (c_ % PR) * 16) = areg[i];                                 \
     }
 
     f32x4 acc[NMAT][4];
@@ -202,24 +192,14 @@ __global__ void __launch_bounds__(kSgThreads, MINW) stream_gemm_kernel(GroupedPa
     // Loads are never skipped (chunk indices are clamped instead): branches
     // around loads would make the compiler's wait-count tracking fall back
     // to draining every outstanding load.
-    // Issue order per chunk: A rows, then weights.  Loads return in issue
-    // order, so storing A of chunk c + 1 (fetched a chunk earlier, ahead of
-    // its weights) waits for nothing newer: the weights of chunks c + 1 and
-    // c + 2 stay in flight across the barrier.
-#if MOE_SG_AHEAD
-    MOE_STREAM_LOAD_A(0, cb);
-    MOE_STREAM_LOAD_B(0, cb);
-    MOE_STREAM_LOAD_A(1, cb + min(1, NC - 1));
-    MOE_STREAM_LOAD_B(1, cb + min(1, NC - 1));
-    MOE_STREAM_STORE_A(0, 0);
-    MOE_BARRIER_LDS();
-#else
+    // Weights of the next chunk are in flight while a chunk is computed; the
+    // group's rows of the next chunk are fetched during the compute and
+    // stored to the other LDS buffer before the barrier.
     MOE_STREAM_LOAD_B(0, cb);
     MOE_STREAM_LOAD_B(1, cb + min(1, NC - 1));
-    MOE_STREAM_LOAD_A(0, cb);
-    MOE_STREAM_STORE_A(0, 0);
+    MOE_STREAM_LOAD_A(cb);
+    MOE_STREAM_STORE_A(0);
     MOE_BARRIER_LDS();
-#endif
 
 #define MOE_STREAM_COMPUTE(BUF_)                                                           \
     {                                                                                      \
@@ -254,33 +234,17 @@ __global__ void __launch_bounds__(kSgThreads, MINW) stream_gemm_kernel(GroupedPa
     }
 
     for (int c = 0; c < NC; c += 2) {
-#if MOE_SG_AHEAD
-      // even chunk: buffers 0
-      MOE_STREAM_COMPUTE(0);
-      MOE_STREAM_LOAD_A(0, cb + min(c + 2, NC - 1));
-      MOE_STREAM_LOAD_B(0, cb + min(c + 2, NC - 1));
-      MOE_STREAM_STORE_A(1, 1);
-      MOE_BARRIER_LDS();
-      if (c + 1 >= NC) break;
-      // odd chunk: buffers 1
-      MOE_STREAM_COMPUTE(1);
-      MOE_STREAM_LOAD_A(1, cb + min(c + 3, NC - 1));
-      MOE_STREAM_LOAD_B(1, cb + min(c + 3, NC - 1));
-      MOE_STREAM_STORE_A(0, 0);
-      MOE_BARRIER_LDS();
-#else
-      MOE_STREAM_LOAD_A(0, cb + min(c + 1, NC - 1));
+      MOE_STREAM_LOAD_A(cb + min(c + 1, NC - 1));
       MOE_STREAM_COMPUTE(0);
       MOE_STREAM_LOAD_B(0, cb + min(c + 2, NC - 1));
-      MOE_STREAM_STORE_A(0, 1);
+      MOE_STREAM_STORE_A(1);
       MOE_BARRIER_LDS();
       if (c + 1 >= NC) break;
-      MOE_STREAM_LOAD_A(0, cb + min(c + 2, NC - 1));
+      MOE_STREAM_LOAD_A(cb + min(c + 2, NC - 1));
       MOE_STREAM_COMPUTE(1);
       MOE_STREAM_LOAD_B(1, cb + min(c + 3, NC - 1));
-      MOE_STREAM_STORE_A(0, 0);
+      MOE_STREAM_STORE_A(0);
       MOE_BARRIER_LDS();
-#endif
     }
 #undef MOE_STREAM_LOAD_A
 #undef MOE_STREAM_STORE_A
