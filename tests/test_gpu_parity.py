@@ -76,11 +76,12 @@ def full_parity(wl, cf=None, label="", w_layout=0):
     return g, ref
 
 
-def sampled_parity(wl, n_tok=192, rows_per_expert=24, seed=0, label=""):
+def sampled_parity(wl, n_tok=192, rows_per_expert=24, seed=0, label="", w_layout=0):
     """Integer stages and the pack in full; floats on sampled rows/tokens."""
-    _say(f"[parity-sampled] {label} cfg{wl.cfg} T={wl.T} d={wl.d} h={wl.h} E={wl.E} k={wl.k}")
+    _say(f"[parity-sampled] {label} cfg{wl.cfg} T={wl.T} d={wl.d} h={wl.h} E={wl.E} k={wl.k} "
+         f"w_layout={w_layout}")
     C = O.capacity(wl.T, wl.k, wl.E, wl.cf)
-    layer, g = run_layer(wl, capacity=C)
+    layer, g = run_layer(wl, capacity=C, w_layout=w_layout)
     x64 = O.to_f64(wl.x, wl.act_dtype)
     wr64 = O.to_f64(wl.w_router, wl.act_dtype)
     r = O.route(x64, wr64, wl.b_router, wl.b_select, wl.k, wl.score, wl.renorm)
@@ -308,20 +309,28 @@ def c1():
     return make_workload(1)
 
 
-def test_c1_full_size(c1):
-    full_parity(c1, label="c1 decode")
+# Full sizes, in the launch configuration bench.py times (tiled weights for
+# the bf16-activation workloads) and on row-major weights.
 
 
-def test_c3_full_size():
-    g, _ = full_parity(make_workload(3), label="c3 switch")
+@pytest.mark.parametrize("w_layout", [0, 1])
+def test_c1_full_size(c1, w_layout):
+    full_parity(c1, label="c1 decode", w_layout=w_layout)
+
+
+@pytest.mark.parametrize("w_layout", [0, 1])
+def test_c3_full_size(w_layout):
+    g, _ = full_parity(make_workload(3), label="c3 switch", w_layout=w_layout)
     assert (g["slot"] < 0).sum() > 0  # the Zipf skew forces drops
 
 
 @pytest.mark.slow
-def test_c2_full_size_sampled():
-    sampled_parity(make_workload(2), label="c2 prefill")
+@pytest.mark.parametrize("w_layout", [0, 1])
+def test_c2_full_size_sampled(w_layout):
+    sampled_parity(make_workload(2), label="c2 prefill", w_layout=w_layout)
 
 
 @pytest.mark.slow
-def test_c4_full_size_sampled():
-    sampled_parity(make_workload(4), label="c4 deepseek share")
+@pytest.mark.parametrize("w_layout", [0, 1])
+def test_c4_full_size_sampled(w_layout):
+    sampled_parity(make_workload(4), label="c4 deepseek share", w_layout=w_layout)
