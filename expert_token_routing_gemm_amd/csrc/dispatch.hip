@@ -31,6 +31,17 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
+// Send-buffer rows are written once and not read again by this kernel's
+// workgroups: nontemporal stores (measured: prefill dispatch 86 -> 76 us,
+// DeepSeek-V3-share dispatch 220 -> 209 us).
+#ifndef MOE_PACK_NT
+#define MOE_PACK_NT 1
+#endif
+__device__ __forceinline__ void store_row16(u32x4* dst, u32x4 v) {
+  if constexpr (MOE_PACK_NT) __builtin_nontemporal_store(v, dst);
+  else *dst = v;
+}
+
 __global__ void __launch_bounds__(kThreads) hist_kernel(const int32_t* __restrict__ ids,
                                                        int32_t* __restrict__ blk, int64_t n_assign,
                                                        int per_block, int E) {
@@ -222,7 +233,7 @@ __global__ void __launch_bounds__(kThreads) rank_pack_kernel(
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
           const int c = c0 + u * 64;
-          if (c < row16) dst[c] = v[u];
+          if (c < row16) store_row16(dst + c, v[u]);
         }
       }
     }
@@ -373,7 +384,7 @@ __global__ void __launch_bounds__(kThreads) pack_kernel(const int32_t* __restric
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
         const int c = c0 + u * kThreads;
-        if (c < row16) dst[c] = v[u];
+        if (c < row16) store_row16(dst + c, v[u]);
       }
     }
   }
