@@ -10,10 +10,15 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = kGemmThreads;
+// Waves per workgroup of the streaming kernel (they share one A staging).
+// The SwiGLU GEMM may use another count that divides its output columns
+// into whole rounds of resident workgroups (see stream_waves).
 #ifndef MOE_SG_WAVES
-#define MOE_SG_WAVES 8  // waves per workgroup of the streaming kernel (share one A staging)
+#define MOE_SG_WAVES 8
 #endif
-constexpr int kSgThreads = 64 * MOE_SG_WAVES;
+#ifndef MOE_SG_WAVES_ALT
+#define MOE_SG_WAVES_ALT 7
+#endif
 
 // ---------------------------------------------------------------- weight streaming
 // Decode-sized groups (at most a few tens of rows per expert) are bound by
@@ -23,7 +28,7 @@ constexpr int kSgThreads = 64 * MOE_SG_WAVES;
 // straight into registers (no LDS), double buffered one K-chunk ahead, with
 // each lane reading CK/2 contiguous bytes of a weight row per chunk.  The
 // group's rows (<= 64 per pass) are staged through LDS once per chunk and
-// shared by the block's 4 waves.  Inside a chunk the lane groups q = lane/16
+// shared by the block's waves.  Inside a chunk the lane groups q = lane/16
 // own disjoint K ranges; the same K permutation is applied to the A
 // fragments read from LDS, so every MFMA still sums over 32 distinct k.
 // Tuning of the weight-streaming kernel: K chunk and minimum waves per SIMD
@@ -64,13 +69,15 @@ __device__ __forceinline__ u32x4 load_stream(const unsigned char* ptr) {
 
 // TL: weights in the 16-row tiled layout (each wave's loads of a chunk are
 // whole contiguous 1 KB pieces; see moe_weight_tile) instead of row-major.
-template <int BSRC, int EPI, int CK, int MINW, bool TL>
-__global__ void __launch_bounds__(kSgThreads, MINW) stream_gemm_kernel(GroupedParams p) {
+template <int BSRC, int EPI, int CK, int MINW, bool TL, int WAVES>
+__global__ void __launch_bounds__(64 * WAVES, MINW) stream_gemm_kernel(GroupedParams p) {
+  constexpr int kSgThreads = 64 * WAVES;
   constexpr int NMAT = (EPI == EPI_SWIGLU) ? 2 : 1;
   constexpr int V = CK / 32;                 // 16-byte bf16 pieces per lane per matrix
   constexpr int RS = CK * 2 + 16;            // LDS row stride (bytes)
   constexpr int MROWS = 64;                  // rows per pass
-  constexpr int A_PIECES = MROWS * CK * 2 / 16 / kSgThreads;  // 16-byte A pieces per thread
+  constexpr int A_TOTAL = MROWS * CK * 2 / 16;  // 16-byte A pieces per chunk
+  constexpr int A_PIECES = (A_TOTAL + kSgThreads - 1) / kSgThreads;  // per thread
   constexpr bool SKIP = (EPI == EPI_SWIGLU) ? MOE_SG_SKIP : MOE_DN_SKIP;
   static_assert(A_PIECES >= 1, "chunk too small");
   static_assert(BSRC != B_FP8 || CK <= 128, "one fp8 scale block per chunk");
@@ -113,7 +120,7 @@ __global__ void __launch_bounds__(kSgThreads, MINW) stream_gemm_kernel(GroupedPa
       Sm[1] = dense ? p.sd3 : (p.s3 ? p.s3 + (int64_t)g * p.ns * p.ks : nullptr);
     }
   }
-  const int ocol0 = blockIdx.x * (16 * MOE_SG_WAVES) + wave * 16;  // first output column of this wave
+  const int ocol0 = blockIdx.x * (16 * WAVES) + wave * 16;  // first output column of this wave
   const int brow = ocol0 + (lane & 15);            // the weight row this lane streams
   const int NC = p.K / CK / p.ksplit;       // chunks of this block's K slice
   const int cb = blockIdx.z * NC;           // first chunk of the slice
@@ -158,17 +165,18 @@ __global__ void __launch_bounds__(kSgThreads, MINW) stream_gemm_kernel(GroupedPa
   for (int m0 = 0; m0 < rows; m0 += MROWS) {
     const int mr = min(MROWS, rows - m0);
     const int mt = (mr + 15) / 16;
-    // A staging: piece c = tid + i*256 of the chunk -> row c / PR, 16-byte
-    // column c % PR.  Every thread loads and stores all its pieces (rows past
-    // the group's end repeat its last row): no divergent branches, so the
-    // compiler can count outstanding loads exactly and the weight prefetch
-    // issued before the A store stays in flight.
+    // A staging: piece c = min(tid + i * threads, A_TOTAL - 1) of the chunk
+    // -> row c / PR, 16-byte column c % PR.  Every thread loads and stores
+    // all its pieces (rows past the group's end repeat its last row; threads
+    // past the last piece repeat it, storing the same bytes): no divergent
+    // branches, so the compiler can count outstanding loads exactly and the
+    // weight prefetch issued before the A store stays in flight.
     constexpr int PR = CK * 2 / 16;
     u32x4 areg[A_PIECES];
     const unsigned char* a_row[A_PIECES];
 #pragma unroll
     for (int i = 0; i < A_PIECES; ++i) {
-      const int c_ = tid + i * kSgThreads;
+      const int c_ = min(tid + i * kSgThreads, A_TOTAL - 1);
       const int rr_ = min(m0 + c_ / PR, rows - 1);
       a_row[i] = reinterpret_cast<const unsigned char*>(A + (int64_t)rr_ * p.K) + (c_ % PR) * 16;
     }
@@ -177,7 +185,7 @@ __global__ void __launch_bounds__(kSgThreads, MINW) stream_gemm_kernel(GroupedPa
       areg[i] = *reinterpret_cast<const u32x4*>(a_row[i] + (int64_t)(C_) * CK * 2);
 #define MOE_STREAM_STORE_A(BUF_)                                                           \
     _Pragma("unroll") for (int i = 0; i < A_PIECES; ++i) {                                 \
-      const int c_ = tid + i * kSgThreads;                                                 \
+      const int c_ = min(tid + i * kSgThreads, A_TOTAL - 1);                               \
       *reinterpret_cast<u32x4*>(lds_a + (BUF_) * MROWS * RS + (c_ / PR) * RS +             \
                                 (c_ % PR) * 16) = areg[i];                                 \
     }
@@ -338,24 +346,55 @@ __global__ void __launch_bounds__(kThreads) splitk_reduce_kernel(GroupedParams p
   *reinterpret_cast<uint2*>(dst) = packed;
 }
 
+// Waves per workgroup of the SwiGLU streaming GEMM.  Each wave streams
+// 16 output columns over the whole K slice, so all workgroups carry the
+// same bytes and a grid that ends in a partial round of resident
+// workgroups leaves slots idle at its end.  The alternative count is taken
+// when it divides the columns and fills its last round better.  Measured on
+// the decode Mixtral layer (h = 14336, 8 experts): 896 workgroups of 8
+// waves are 1.75 rounds of 2 per CU, 1024 of 7 waves exactly 2; GEMM 1
+// takes 308 instead of 329 us (14-wave workgroups, 1 round: 318 us).
+#ifndef MOE_SG_WAVES_RULE
+#define MOE_SG_WAVES_RULE 1
+#endif
+int stream_waves(int out_cols, int ngroups, int ksplit) {
+  if (!MOE_SG_WAVES_RULE || out_cols % (16 * MOE_SG_WAVES_ALT) != 0) return MOE_SG_WAVES;
+  if (MOE_SG_WAVES_RULE == 2) return MOE_SG_WAVES_ALT;
+  const int64_t slots_per_cu = 4 * MOE_SG_MINW;  // resident waves per CU at the VGPR budget
+  const int64_t cus = device_info().cus;
+  auto frac_tail = [&](int w) {  // fraction of the last round's slots that are busy
+    const int64_t per = cus * (slots_per_cu / w);
+    const int64_t wg = (int64_t)out_cols / (16 * w) * ngroups * ksplit;
+    const int64_t r = wg % per;
+    return r == 0 ? 1.0 : (double)r / per;
+  };
+  return frac_tail(MOE_SG_WAVES_ALT) > frac_tail(MOE_SG_WAVES) ? MOE_SG_WAVES_ALT : MOE_SG_WAVES;
+}
+
+template <int BSRC, int EPI, int CK, int WAVES>
+moe_status launch_stream_w(const GroupedParams& p, int ngroups, int out_cols, hipStream_t stream) {
+  constexpr int MW = EPI == EPI_SWIGLU ? MOE_SG_MINW : MOE_DN_MINW;
+  auto kern = p.b_tiled ? stream_gemm_kernel<BSRC, EPI, CK, MW, true, WAVES>
+                        : stream_gemm_kernel<BSRC, EPI, CK, MW, false, WAVES>;
+  constexpr size_t lds = 2 * 64 * (CK * 2 + 16);
+  static_assert(lds <= 64 * 1024, "within the default LDS limit");
+  dim3 grid(out_cols / (16 * WAVES), ngroups, p.ksplit);
+  kern<<<grid, 64 * WAVES, lds, stream>>>(p);
+  MOE_CHECK_LAUNCH();
+  return MOE_OK;
+}
+
 template <int BSRC, int EPI, int CK>
 moe_status launch_stream(const GroupedParams& p, hipStream_t stream) {
-  constexpr int MW = EPI == EPI_SWIGLU ? MOE_SG_MINW : MOE_DN_MINW;
-  auto kern = p.b_tiled ? stream_gemm_kernel<BSRC, EPI, CK, MW, true>
-                        : stream_gemm_kernel<BSRC, EPI, CK, MW, false>;
-  constexpr size_t lds = 2 * 64 * (CK * 2 + 16);
-  static bool attr_set[2] = {false, false};
-  if (!attr_set[p.b_tiled ? 1 : 0]) {
-    MOE_CHECK_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                      (int)lds));
-    attr_set[p.b_tiled ? 1 : 0] = true;
-  }
   const int ngroups = p.n_routed + (p.t_dense > 0 ? 1 : 0);
   const int out_cols = (EPI == EPI_SWIGLU) ? p.N / 2 : p.N;
   if (ngroups == 0) return MOE_OK;
-  dim3 grid(out_cols / (16 * MOE_SG_WAVES), ngroups, p.ksplit);
-  kern<<<grid, kSgThreads, lds, stream>>>(p);
-  MOE_CHECK_LAUNCH();
+  moe_status st;
+  if (EPI == EPI_SWIGLU && stream_waves(out_cols, ngroups, p.ksplit) == MOE_SG_WAVES_ALT)
+    st = launch_stream_w<BSRC, EPI, CK, MOE_SG_WAVES_ALT>(p, ngroups, out_cols, stream);
+  else
+    st = launch_stream_w<BSRC, EPI, CK, MOE_SG_WAVES>(p, ngroups, out_cols, stream);
+  if (st != MOE_OK) return st;
   if (p.ksplit > 1) {
     const int64_t n4 = p.prow_total * (out_cols / 4);
     splitk_reduce_kernel<EPI><<<(int)((n4 + kThreads - 1) / kThreads), kThreads, 0, stream>>>(

@@ -121,6 +121,8 @@ def sampled_parity(wl, n_tok=192, rows_per_expert=24, seed=0, label="", w_layout
 SMALL = {
     "c0-ragged": (0, dict(T=1000, d=256, h=384)),
     "c1-small": (1, dict(T=40, d=512, h=768)),
+    # h a multiple of 7 * 128: the SwiGLU streaming GEMM takes 7-wave workgroups
+    "c1-seven-wave": (1, dict(T=40, d=512, h=896)),
     "c2-small": (2, dict(T=1000, d=512, h=640)),
     "c3-small": (3, dict(T=4096, d=256, h=512)),
     "c4-small": (4, dict(T=256, d=512, h=256)),
@@ -226,6 +228,7 @@ TILED = {
     # streaming path
     "c1-small": (1, dict(T=40, d=512, h=768)),
     "c1-tiny-ragged": (1, dict(T=5, d=256, h=384)),
+    "c1-seven-wave": (1, dict(T=40, d=512, h=896)),
     "c4-decode": (4, dict(T=48, d=512, h=256)),
     # LDS-DMA path: bf16 and fp8 weights, 128- and 256-row tiles
     "c2-small": (2, dict(T=1000, d=512, h=640)),
