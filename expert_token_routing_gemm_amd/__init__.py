@@ -298,7 +298,8 @@ class MoELayer:
 
     def forward(self, events=None, stream=None):
         """Whole layer; ``events`` = list of MOE_LAYER_EVENTS raw hipEvent_t
-        handles (ints) recorded at the stage boundaries, or None."""
+        handles (ints; None skips that boundary) recorded at the stage
+        boundaries, or None."""
         if events is not None:
             arr = (C.c_void_p * MOE_LAYER_EVENTS)(*events)
             self.args.events = C.cast(arr, C.POINTER(C.c_void_p))

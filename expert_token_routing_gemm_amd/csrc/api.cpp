@@ -98,18 +98,18 @@ extern "C" moe_status moe_layer_forward(const moe_layer_args* a, void* ws, size_
     return MOE_ERR_WORKSPACE;
   }
   hipEvent_t* ev = a->events;
-  if (ev) MOE_CHECK_HIP(hipEventRecord(ev[0], stream));
+  if (ev && ev[0]) MOE_CHECK_HIP(hipEventRecord(ev[0], stream));
   moe_status st = moe_route(&a->route, ws, ws_bytes, stream);
   if (st != MOE_OK) return st;
-  if (ev) MOE_CHECK_HIP(hipEventRecord(ev[1], stream));
+  if (ev && ev[1]) MOE_CHECK_HIP(hipEventRecord(ev[1], stream));
   st = moe_dispatch(&a->dispatch, ws, ws_bytes, stream);
   if (st != MOE_OK) return st;
-  if (ev) MOE_CHECK_HIP(hipEventRecord(ev[2], stream));
+  if (ev && ev[2]) MOE_CHECK_HIP(hipEventRecord(ev[2], stream));
   st = expert_ffn_impl(&a->ffn, ws, ws_bytes, stream, ev ? ev[3] : nullptr);
   if (st != MOE_OK) return st;
-  if (ev) MOE_CHECK_HIP(hipEventRecord(ev[4], stream));
+  if (ev && ev[4]) MOE_CHECK_HIP(hipEventRecord(ev[4], stream));
   st = moe_combine(&a->combine, stream);
   if (st != MOE_OK) return st;
-  if (ev) MOE_CHECK_HIP(hipEventRecord(ev[5], stream));
+  if (ev && ev[5]) MOE_CHECK_HIP(hipEventRecord(ev[5], stream));
   return MOE_OK;
 }

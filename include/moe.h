@@ -277,14 +277,17 @@ moe_status moe_combine(const moe_combine_args* a, hipStream_t stream);
  * host synchronisation.  The four argument blocks must be consistent (the
  * caller wires ids, slot, x_send, ... between them).  If `events` is not
  * NULL it holds MOE_LAYER_EVENTS host-side hipEvent_t handles, recorded at
- * the stage boundaries listed at MOE_LAYER_EVENTS.
+ * the stage boundaries listed at MOE_LAYER_EVENTS; a NULL entry is skipped.
+ * Each recorded event delays the next kernel's start by a few microseconds,
+ * so a caller timing one stage passes only the two events around it.
  */
 typedef struct moe_layer_args {
   moe_route_args route;
   moe_dispatch_args dispatch;
   moe_ffn_args ffn;
   moe_combine_args combine;
-  hipEvent_t* events;     /* host array of MOE_LAYER_EVENTS events, or NULL */
+  hipEvent_t* events;     /* host array of MOE_LAYER_EVENTS events (entries may
+                             be NULL), or NULL */
 } moe_layer_args;
 
 size_t moe_workspace_bytes(const moe_layer_args* a);

@@ -371,3 +371,49 @@ def test_layer_forward_in_hip_graph(cfg, over, w_layout):
         torch.cuda.synchronize()
         for k, v in ref.items():
             np.testing.assert_array_equal(to_host(getattr(layer, k)), v, err_msg=k)
+
+
+def _hip_runtime():
+    """The HIP runtime torch already loaded (for raw hipEvent_t handles)."""
+    import ctypes
+    path = next((ln.split()[-1] for ln in open("/proc/self/maps") if "libamdhip64" in ln), None)
+    h = ctypes.CDLL(path or "libamdhip64.so")
+    h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return h
+
+
+def test_layer_forward_partial_events():
+    """NULL entries of the event array are skipped: recording only the two
+    events around the first expert GEMM times it and changes no result."""
+    import ctypes
+
+    from expert_token_routing_gemm_amd import MOE_LAYER_EVENTS, MoELayer, to_host
+    wl = make_workload(1, T=64, d=512, h=768)
+    _say("[events] cfg1 T=64, events at the first GEMM only")
+    layer = MoELayer(wl, w_layout=1)
+    layer.forward()
+    ref = {k: to_host(getattr(layer, k)) for k in ("y", "ids", "slot", "counts")}
+    hip = _hip_runtime()
+    evs = []
+    for _ in range(2):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        evs.append(e.value)
+    try:
+        arr = [None] * MOE_LAYER_EVENTS
+        arr[2], arr[3] = evs
+        for k in ("y", "ids", "slot", "counts"):
+            getattr(layer, k).zero_()
+        layer.forward(events=arr)
+        torch.cuda.synchronize()
+        ms = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), evs[0], evs[1]) == 0
+        assert ms.value > 0
+        for k, v in ref.items():
+            np.testing.assert_array_equal(to_host(getattr(layer, k)), v, err_msg=k)
+    finally:
+        for e in evs:
+            hip.hipEventDestroy(e)
