@@ -10,7 +10,8 @@
 // buffer-management bullet), which also fixes which assignments are dropped:
 // the ones past the first C in token-major order.
 //
-// Three kernels, no ordering atomics (results are deterministic):
+// Large batches: three kernels, no ordering atomics (results are
+// deterministic); small and tiny batches: see below.
 //   hist_kernel      : block b owns a chunk of TB tokens (TB*k <= 256
 //                      assignments); LDS-private histogram -> blk[b][e].
 //   scan_kernel      : one workgroup; per expert an exclusive scan over blocks
@@ -390,6 +391,137 @@ __global__ void __launch_bounds__(kThreads) pack_kernel(const int32_t* __restric
   }
 }
 
+// Tiny batches (T*k <= kTinyAssign, decode): one launch.  Every workgroup
+// owns one token and recomputes the whole plan it needs from all the ids
+// (at most kTinyAssign of them, read once into LDS): the per-expert
+// histogram and offsets, and for each of its assignments the number of
+// earlier assignments (token-major order) to the same expert, which is its
+// position in that expert's segment.  Workgroup 0 also writes the counts
+// and offsets.  The redundant plan costs a few microseconds of latency that
+// overlaps the row copies; it saves the separate single-workgroup launch.
+constexpr int kTinyAssign = 1024;
+
+__global__ void __launch_bounds__(kThreads) plan_pack_tiny_kernel(
+    const int32_t* __restrict__ ids, int64_t T, int k, int E, int R, int C,
+    int32_t* __restrict__ counts, int32_t* __restrict__ kept, int32_t* __restrict__ off,
+    int32_t* __restrict__ rank_counts, int32_t* __restrict__ rank_off,
+    int32_t* __restrict__ slot_out, int32_t* __restrict__ src_out, const u32x4* __restrict__ x,
+    u32x4* __restrict__ x_send, int row16) {
+  __shared__ int s_ids[kTinyAssign];
+  __shared__ int cnt[MOE_MAX_EXPERTS];
+  __shared__ int offs[MOE_MAX_EXPERTS + 1];
+  __shared__ int wsum[kWaves];
+  __shared__ int part[kWaves][MOE_MAX_TOPK];
+  __shared__ int s_slot[MOE_MAX_TOPK];
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int w = tid / 64;
+  const int64_t t = blockIdx.x;
+  const int n = (int)(T * k);
+  for (int e = tid; e < MOE_MAX_EXPERTS; e += kThreads) cnt[e] = 0;
+  for (int g = tid; g < n; g += kThreads) s_ids[g] = ids[g];
+  __syncthreads();
+  for (int g = tid; g < n; g += kThreads) {
+    const int e = s_ids[g];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  // exclusive scan of kept over the experts (one expert per thread)
+  const int kp = tid < E ? min(cnt[tid], C) : 0;
+  int incl = kp;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  for (int i = 0; i < w; ++i) incl += wsum[i];
+  if (tid < E) offs[tid] = incl - kp;
+  if (tid == E - 1) offs[E] = incl;
+  if (t == 0 && tid < E) {
+    counts[tid] = cnt[tid];
+    kept[tid] = kp;
+    off[tid] = incl - kp;
+  }
+  if (t == 0 && tid == E - 1) off[E] = incl;
+  // earlier assignments to the same expert, for each of this token's k
+  const int64_t first = t * k;
+  int my_e[MOE_MAX_TOPK];
+  int c[MOE_MAX_TOPK];
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    my_e[j] = j < k ? s_ids[first + j] : -1;
+    c[j] = 0;
+  }
+  for (int g = tid; g < n; g += kThreads) {
+    const int e = s_ids[g];
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) c[j] += (g < first + j && e == my_e[j]) ? 1 : 0;
+  }
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) c[j] += __shfl_xor(c[j], o, 64);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) part[w][j] = c[j];
+  }
+  __syncthreads();
+  if (t == 0) {
+    const int per = E / R;
+    for (int r = tid; r < R; r += kThreads) {
+      rank_counts[r] = offs[(r + 1) * per] - offs[r * per];
+      rank_off[r] = offs[r * per];
+    }
+    if (tid == 0) rank_off[R] = offs[E];
+  }
+  if (tid < k) {
+    const int e = my_e[tid];
+    int pos = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) pos += part[i][tid];
+    int sl = -1;
+    if (e >= 0 && e < E && pos < C) {
+      sl = offs[e] + pos;
+      src_out[sl] = (int32_t)t;
+    }
+    slot_out[first + tid] = sl;
+    s_slot[tid] = sl;
+  }
+  __syncthreads();
+  // the row, read once, to each kept slot
+  int sj[MOE_MAX_TOPK];
+  bool any = false;
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    sj[j] = j < k ? s_slot[j] : -1;
+    any |= sj[j] >= 0;
+  }
+  if (!any) return;
+  const u32x4* xr = x + t * row16;
+  constexpr int UNROLL = 2;
+  for (int c0 = tid; c0 < row16; c0 += kThreads * UNROLL) {
+    u32x4 v[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const int cc = c0 + u * kThreads;
+      if (cc < row16) v[u] = xr[cc];
+    }
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      if (sj[j] < 0) continue;
+      u32x4* dst = x_send + (int64_t)sj[j] * row16;
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const int cc = c0 + u * kThreads;
+        if (cc < row16) store_row16(dst + cc, v[u]);
+      }
+    }
+  }
+}
+
 struct Plan {
   int tokens_per_block;
   int nblocks;
@@ -446,6 +578,16 @@ extern "C" moe_status moe_dispatch(const moe_dispatch_args* a, void* ws, size_t 
   if (need > 0 && (ws_bytes < need || ws == nullptr)) {
     set_error("moe_dispatch: workspace too small");
     return MOE_ERR_WORKSPACE;
+  }
+#ifndef MOE_DISPATCH_TINY
+#define MOE_DISPATCH_TINY 1
+#endif
+  if (MOE_DISPATCH_TINY && a->T > 0 && a->T * a->k <= kTinyAssign) {
+    plan_pack_tiny_kernel<<<(int)a->T, kThreads, 0, stream>>>(
+        a->ids, a->T, a->k, a->E, a->R, a->capacity, a->counts, a->kept, a->expert_off,
+        a->rank_counts, a->rank_off, a->slot, a->src, (const u32x4*)a->x, (u32x4*)a->x_send, row16);
+    MOE_CHECK_LAUNCH();
+    return MOE_OK;
   }
   if (a->T > 0 && a->T * a->k <= kSmallAssign) {
     plan_small_kernel<<<1, kSmallThreads, 0, stream>>>(
