@@ -258,18 +258,24 @@ __global__ void __launch_bounds__(256) route_decode_kernel(
   float acc[EMAX];
 #pragma unroll
   for (int e = 0; e < EMAX; ++e) acc[e] = 0.f;
+  // All loads of a chunk are issued before any is used and none sits behind a
+  // branch (experts past E re-read row E-1; their sums are never used), so
+  // they are in flight together instead of one L2 round trip each.
 #pragma unroll 2
   for (int c = threadIdx.x; c < nchunk; c += 256) {
+    const u32x4 xr = *reinterpret_cast<const u32x4*>(x + t * d + (int64_t)c * VN);
+    u32x4 wraw[EMAX];
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e)
+      wraw[e] = *reinterpret_cast<const u32x4*>(wr + (int64_t)min(e, E - 1) * d + (int64_t)c * VN);
     float xv[VN];
-    Vec16<T>::load(x + t * d + (int64_t)c * VN, xv);
+    Vec16<T>::widen(xr, xv);
 #pragma unroll
     for (int e = 0; e < EMAX; ++e) {
-      if (e < E) {
-        float wv[VN];
-        Vec16<T>::load(wr + (int64_t)e * d + (int64_t)c * VN, wv);
+      float wv[VN];
+      Vec16<T>::widen(wraw[e], wv);
 #pragma unroll
-        for (int v = 0; v < VN; ++v) acc[e] = fmaf(xv[v], wv[v], acc[e]);
-      }
+      for (int v = 0; v < VN; ++v) acc[e] = fmaf(xv[v], wv[v], acc[e]);
     }
   }
 #pragma unroll
@@ -317,27 +323,27 @@ __global__ void __launch_bounds__(256) logits_valu_kernel(const T* __restrict__ 
 #pragma unroll
       for (int e = 0; e < ES; ++e) acc[i][e] = 0.f;
     for (int c = lane; c < nchunk; c += kWave) {
+      // every load of the chunk in flight at once: tokens past T and experts
+      // past E re-read the last row (their sums are never stored)
+      u32x4 xr[TPW], wraw[ES];
+#pragma unroll
+      for (int i = 0; i < TPW; ++i)
+        xr[i] = *reinterpret_cast<const u32x4*>(x + min(t0 + i, T_tok - 1) * d + (int64_t)c * VN);
+#pragma unroll
+      for (int e = 0; e < ES; ++e)
+        wraw[e] = *reinterpret_cast<const u32x4*>(wr + (int64_t)min(e0 + e, E - 1) * d +
+                                                  (int64_t)c * VN);
       float xv[TPW][VN];
 #pragma unroll
-      for (int i = 0; i < TPW; ++i) {
-        const int64_t t = t0 + i;
-        if (t < T_tok) {
-          Vec16<T>::load(x + t * d + (int64_t)c * VN, xv[i]);
-        } else {
-#pragma unroll
-          for (int v = 0; v < VN; ++v) xv[i][v] = 0.f;
-        }
-      }
+      for (int i = 0; i < TPW; ++i) Vec16<T>::widen(xr[i], xv[i]);
 #pragma unroll
       for (int e = 0; e < ES; ++e) {
-        if (e0 + e < E) {
-          float wv[VN];
-          Vec16<T>::load(wr + (int64_t)(e0 + e) * d + (int64_t)c * VN, wv);
+        float wv[VN];
+        Vec16<T>::widen(wraw[e], wv);
 #pragma unroll
-          for (int i = 0; i < TPW; ++i)
+        for (int i = 0; i < TPW; ++i)
 #pragma unroll
-            for (int v = 0; v < VN; ++v) acc[i][e] = fmaf(xv[i][v], wv[v], acc[i][e]);
-        }
+          for (int v = 0; v < VN; ++v) acc[i][e] = fmaf(xv[i][v], wv[v], acc[i][e]);
       }
     }
 #pragma unroll
@@ -423,13 +429,19 @@ __device__ __forceinline__ void group_limit(float (&key)[MOE_MAX_EXPERTS / kWave
   }
 }
 
-// logits_in holds ks slices [ks][T][E] of partial sums, added in slice order.
+// logits_in holds KS slices [KS][T][E] of partial sums, added in slice order.
+// PERN: experts per lane actually present (ceil(E / 64)).  All KS * PERN
+// loads of a token are issued together, unconditionally (experts past E
+// re-read expert E-1 and are ignored), so they overlap instead of each
+// waiting for the previous one.
+template <int PERN, int KS>
 __global__ void __launch_bounds__(256) topk_kernel(
-    const float* __restrict__ logits_in, int ks, const float* __restrict__ b_router,
+    const float* __restrict__ logits_in, const float* __restrict__ b_router,
     const float* __restrict__ b_select, float* __restrict__ logits_out, int32_t* __restrict__ ids,
     float* __restrict__ weights, int64_t T_tok, int E, int k, int score, int renorm, int ng,
     int tg) {
   constexpr int PER = MOE_MAX_EXPERTS / kWave;  // 4
+  static_assert(PERN >= 1 && PERN <= PER, "experts per lane");
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
   const int64_t waves_total = (int64_t)gridDim.x * (blockDim.x / kWave);
@@ -437,6 +449,13 @@ __global__ void __launch_bounds__(256) topk_kernel(
        t += waves_total) {
     float L[PER], key[PER], sc[PER];
     bool taken[PER];
+    float part[PERN][KS];
+#pragma unroll
+    for (int i = 0; i < PERN; ++i) {
+      const int ec = min(lane + i * kWave, E - 1);
+#pragma unroll
+      for (int z = 0; z < KS; ++z) part[i][z] = logits_in[(int64_t)z * T_tok * E + t * E + ec];
+    }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int e = lane + i * kWave;
@@ -444,9 +463,10 @@ __global__ void __launch_bounds__(256) topk_kernel(
       L[i] = -INFINITY;
       key[i] = -INFINITY;
       sc[i] = 0.f;
-      if (e < E) {
-        float l = logits_in[t * E + e];
-        for (int z = 1; z < ks; ++z) l += logits_in[(int64_t)z * T_tok * E + t * E + e];
+      if (i < PERN && e < E) {
+        float l = part[i < PERN ? i : 0][0];
+#pragma unroll
+        for (int z = 1; z < KS; ++z) l += part[i < PERN ? i : 0][z];
         L[i] = l + (b_router ? b_router[e] : 0.f);
         if (logits_out) logits_out[t * E + e] = L[i];
         if (score == MOE_SIGMOID) {
@@ -522,6 +542,42 @@ __global__ void __launch_bounds__(256) topk_kernel(
   }
 }
 
+int grid_for(int64_t units, int per_block);
+
+template <int PERN>
+bool launch_topk_p(const float* in, int ks, const moe_route_args* a, const float* b_router,
+                   float* logits_out, int ng, hipStream_t stream) {
+  const dim3 grid(grid_for(a->T, 4)), tb(256);
+  const int tg = a->topk_groups;
+  switch (ks) {
+#define MOE_TOPK_CASE(K_)                                                                    \
+  case K_:                                                                                 \
+    topk_kernel<PERN, K_><<<grid, tb, 0, stream>>>(in, b_router, a->b_select, logits_out,  \
+                                                   a->ids, a->weights, a->T, a->E, a->k,   \
+                                                   a->score, a->renorm, ng, tg);           \
+    break;
+    MOE_TOPK_CASE(1)
+    MOE_TOPK_CASE(2)
+    MOE_TOPK_CASE(4)
+    MOE_TOPK_CASE(8)
+    MOE_TOPK_CASE(16)
+#undef MOE_TOPK_CASE
+    default:
+      return false;
+  }
+  return true;
+}
+
+// Scores and top-k from ks slices of logits; false (nothing launched) unless
+// ks is a power of two <= 16.
+bool launch_topk(const float* in, int ks, const moe_route_args* a, const float* b_router,
+                 float* logits_out, int ng, hipStream_t stream) {
+  const int pern = (a->E + kWave - 1) / kWave;
+  if (pern <= 1) return launch_topk_p<1>(in, ks, a, b_router, logits_out, ng, stream);
+  if (pern <= 2) return launch_topk_p<2>(in, ks, a, b_router, logits_out, ng, stream);
+  return launch_topk_p<4>(in, ks, a, b_router, logits_out, ng, stream);
+}
+
 int grid_for(int64_t units, int per_block) {
   const int64_t want = (units + per_block - 1) / per_block;
   const int64_t cap = (int64_t)device_info().cus * 8;
@@ -583,10 +639,10 @@ extern "C" moe_status moe_route(const moe_route_args* a, void* ws, size_t ws_byt
   if (a->x == nullptr) {
     MOE_CHECK_ARG(a->logits != nullptr, "x == NULL needs input logits");
     MOE_CHECK_ARG(a->b_router == nullptr, "x == NULL: logits are final, b_router must be NULL");
-    topk_kernel<<<grid_for(a->T, 4), tb, 0, stream>>>(a->logits, 1, nullptr, a->b_select, nullptr,
-                                                       a->ids, a->weights, a->T, a->E, a->k,
-                                                       a->score, a->renorm,
-                                                       grouped(a) ? a->n_groups : 0, a->topk_groups);
+    if (!launch_topk(a->logits, 1, a, nullptr, nullptr, grouped(a) ? a->n_groups : 0, stream)) {
+      set_error("moe_route: unsupported split of the router logits");
+      return MOE_ERR_INVALID;
+    }
     MOE_CHECK_LAUNCH();
     return MOE_OK;
   }
@@ -650,10 +706,10 @@ extern "C" moe_status moe_route(const moe_route_args* a, void* ws, size_t ws_byt
     }
     MOE_CHECK_LAUNCH();
   }
-  topk_kernel<<<grid_for(a->T, 4), tb, 0, stream>>>(raw, ks, a->b_router, a->b_select, a->logits,
-                                                     a->ids, a->weights, a->T, a->E, a->k,
-                                                     a->score, a->renorm,
-                                                     grouped(a) ? a->n_groups : 0, a->topk_groups);
+  if (!launch_topk(raw, ks, a, a->b_router, a->logits, grouped(a) ? a->n_groups : 0, stream)) {
+    set_error("moe_route: unsupported split of the router logits");
+    return MOE_ERR_INVALID;
+  }
   MOE_CHECK_LAUNCH();
   return MOE_OK;
 }

@@ -124,6 +124,10 @@ SMALL = {
     # h a multiple of 7 * 128: the SwiGLU streaming GEMM takes 7-wave workgroups
     "c1-seven-wave": (1, dict(T=40, d=512, h=896)),
     "c2-small": (2, dict(T=1000, d=512, h=640)),
+    # E = 16: above the small-router limit and not a multiple of 64, so the
+    # logits come from the VALU kernel (bf16 and fp32) before the top-k kernel
+    "c3-valu-router": (3, dict(T=1000, d=256, h=512, E=16)),
+    "c0-valu-router": (0, dict(T=600, d=256, h=256, E=16)),
     "c3-small": (3, dict(T=4096, d=256, h=512)),
     "c4-small": (4, dict(T=256, d=512, h=256)),
     # just above the single-workgroup dispatch limit (T*k > 4096): multi-block path

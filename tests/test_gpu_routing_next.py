@@ -120,6 +120,31 @@ def test_grouped_full_layer(ng, tg):
     _say(f"[grouped layer] ok: y err {e_y:.2e}, near-tie tokens {int(diff.sum())}")
 
 
+def test_grouped_full_layer_valu_router():
+    """Group-limited routing on an 8-expert layer: the logits come from the
+    VALU router kernel, then the grouped top-k."""
+    from expert_token_routing_gemm_amd import MoELayer, to_host
+    wl = make_workload(2, T=300, d=256, h=256)
+    ng, tg = 4, 2
+    _say(f"[grouped layer valu] T={wl.T} E={wl.E} ng={ng} tg={tg}")
+    C = O.capacity(wl.T, wl.k, wl.E, wl.cf)
+    layer = MoELayer(wl, capacity=C, n_groups=ng, topk_groups=tg)
+    layer.forward()
+    g = layer.results()
+    ref = O.layer(wl, n_groups=ng, topk_groups=tg)
+    exempt = ref["route"]["gap"] < P.NEAR_TIE
+    diff = np.any(g["ids"] != ref["route"]["ids"], axis=1)
+    assert not (diff & ~exempt).any()
+    assert max(len(set((row // (wl.E // ng)).tolist())) for row in g["ids"]) <= tg
+    if diff.any():
+        ref = O.layer(wl, ids_override=g["ids"], n_groups=ng, topk_groups=tg)
+    P.check_dispatch(wl, g, g["ids"], C)
+    np.testing.assert_allclose(g["weights"], ref["route"]["weights"], rtol=0, atol=5e-5)
+    y = to_host(layer.y)
+    e_y = P.check_close("y", P.act_to_f64(y, wl.act_dtype), ref["y"], P.tol_of(wl))
+    _say(f"[grouped layer valu] ok: y err {e_y:.2e}")
+
+
 def test_grouped_rejects_bad_arguments():
     from expert_token_routing_gemm_amd import MoELayer
     wl = make_workload(4, T=64, d=256, h=256)
