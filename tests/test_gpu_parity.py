@@ -123,6 +123,10 @@ SMALL = {
     "c1-small": (1, dict(T=40, d=512, h=768)),
     # h a multiple of 7 * 128: the SwiGLU streaming GEMM takes 7-wave workgroups
     "c1-seven-wave": (1, dict(T=40, d=512, h=896)),
+    # d = h = 384 (six 64-element chunks): both streaming GEMMs split K into
+    # exactly two slices; the skewed case has experts past 64 rows
+    "c1-k-split-2": (1, dict(T=40, d=384, h=384)),
+    "c2-decode-skewed-k-split-2": (2, dict(T=256, d=384, h=384)),
     "c2-small": (2, dict(T=1000, d=512, h=640)),
     # E = 16: above the small-router limit and not a multiple of 64, so the
     # logits come from the VALU kernel (bf16 and fp32) before the top-k kernel
@@ -233,6 +237,7 @@ TILED = {
     "c1-small": (1, dict(T=40, d=512, h=768)),
     "c1-tiny-ragged": (1, dict(T=5, d=256, h=384)),
     "c1-seven-wave": (1, dict(T=40, d=512, h=896)),
+    "c1-k-split-2": (1, dict(T=40, d=384, h=384)),
     "c4-decode": (4, dict(T=48, d=512, h=256)),
     # LDS-DMA path: bf16 and fp8 weights, 128- and 256-row tiles
     "c2-small": (2, dict(T=1000, d=512, h=640)),
