@@ -19,6 +19,7 @@ import json
 import os
 import sys
 import time
+import types
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -200,6 +201,33 @@ def copy_probe(mib: int, steps: int):
     print(json.dumps({"copy_probe_mib": mib, **out}), flush=True)
 
 
+def dense_reference(wl, steps: int):
+    """The vendor library's rate on one dense GEMM with the flops of the
+    workload's first expert GEMM at even routing: rows = the executed
+    experts' share of the T*k assignments (plus T for a shared expert),
+    N = n*h, K = d, bf16, one torch.matmul on the nn.Linear layout.  A
+    reference point for the grouped kernels, not part of the layer."""
+    import torch
+    n1 = 2 if wl.act == "swiglu" else 1
+    M = wl.T * wl.k * (wl.e_end - wl.e_begin) // wl.E + (wl.T if wl.shared else 0)
+    N, K = n1 * wl.h, wl.d
+    a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(N, K, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        c = a @ b.t()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        c = a @ b.t()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    del c
+    print(json.dumps({"dense_reference": f"torch.matmul bf16 [{M},{K}] x [{K},{N}]", "ms": ms,
+                      "tflops": 2.0 * M * N * K / ms / 1e9}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -215,6 +243,9 @@ def main():
                     help="after the timed region: route -> dispatch -> bias update steps on "
                          "workloads with a selection bias (reports max/mean expert load)")
     ap.add_argument("--balance-gamma", type=float, default=0.01)
+    ap.add_argument("--dense-reference", action="store_true",
+                    help="instead of the layer: time torch.matmul (the vendor BLAS) on the dense "
+                         "bf16 GEMM with the first expert GEMM's flops")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead of the layer: time a plain device copy of MIB MiB (HBM "
                          "calibration for the traffic counters) and a full read (sum)")
@@ -234,6 +265,10 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_probe:
         copy_probe(args.copy_probe, args.steps)
+        return
+    if args.dense_reference:
+        from synth.gen import CONFIGS
+        dense_reference(types.SimpleNamespace(**CONFIGS[args.config]), args.steps)
         return
     print(f"[bench] generating workload {args.config}", file=sys.stderr, flush=True)
     wl = make_workload(args.config)

@@ -485,11 +485,17 @@ moe_status launch_dma(const GroupedParams& p, int64_t max_routed_rows, hipStream
 #ifndef MOE_DMA_BIG_WN
 #define MOE_DMA_BIG_WN 4
 #endif
+#ifndef MOE_DMA_SMALL_ROWS
+#define MOE_DMA_SMALL_ROWS 768
+#endif
+#ifndef MOE_DMA_FP8_BIG
+#define MOE_DMA_FP8_BIG 0
+#endif
 template <int BSRC, bool TL, int EPI>
 moe_status launch_dma_shape(const GroupedParams& p, int64_t max_routed_rows, hipStream_t s) {
   const int groups = p.n_routed > 0 ? p.n_routed : 1;
-  const bool small_tiles =
-      BSRC == B_FP8 || (p.t_dense == 0 && max_routed_rows / groups < 768);
+  const bool small_tiles = (BSRC == B_FP8 && !MOE_DMA_FP8_BIG) ||
+                           (p.t_dense == 0 && max_routed_rows / groups < MOE_DMA_SMALL_ROWS);
   if (small_tiles) return launch_dma<BSRC, TL, EPI, 128, 256, 1, 4, 3, 2>(p, max_routed_rows, s);
   return launch_dma<BSRC, TL, EPI, 256, 256, 2, MOE_DMA_BIG_WN>(p, max_routed_rows, s);
 }
