@@ -481,7 +481,9 @@ moe_status launch_dma(const GroupedParams& p, int64_t max_routed_rows, hipStream
 // fp8 weights (their B stage is half as large, so the second workgroup's
 // extra operand traffic costs less).  Measured: Switch workload 1.00 ->
 // 0.87 ms, DeepSeek-V3 share 1.78 -> 1.67 ms; the bf16 prefill workload stays
-// faster on 256x256 (11.8 vs 13.0 ms).
+// faster on 256x256 (11.8 vs 13.0 ms).  Knobs: waves along N of the 256x256
+// tile, the mean rows per group below which 128x256 tiles are used, and
+// whether fp8 weights may take 256x256 tiles (measured slower: 6-22%).
 #ifndef MOE_DMA_BIG_WN
 #define MOE_DMA_BIG_WN 4
 #endif

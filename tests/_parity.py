@@ -1,11 +1,11 @@
 """Shared helpers of the GPU parity tests: run the HIP path through the C ABI
-and judge it against the fp64 oracle.
+and compare it with the fp64 oracle.
 
 Tolerances (max-abs error normalised by the row max, on the expert outputs
 before combine and on the layer output): fp32 1e-4, bf16 2e-2, fp8 weights
 6e-2.  Integer outputs must match bit for bit.  Route ids may differ only on
 tokens whose oracle score gap between the k-th and (k+1)-th expert is below
-1e-6; integer stages are then judged against the oracle replayed on the GPU's
+1e-6; integer stages are then compared with the oracle replayed on the GPU's
 ids.
 """
 from __future__ import annotations
