@@ -241,19 +241,27 @@ __global__ void __launch_bounds__(64 * WAVES, MINW) stream_gemm_kernel(GroupedPa
       }                                                                                    \
     }
 
-    for (int c = 0; c < NC; c += 2) {
-      MOE_STREAM_LOAD_A(cb + min(c + 1, NC - 1));
+    // Steady state: every weight load is a chunk still to be computed (an odd
+    // chunk count re-reads its last chunk once); the last one or two chunks
+    // are computed after the loop without further weight loads.
+    int c = 0;
+    for (; c + 2 < NC; c += 2) {
+      MOE_STREAM_LOAD_A(cb + c + 1);
       MOE_STREAM_COMPUTE(0);
-      MOE_STREAM_LOAD_B(0, cb + min(c + 2, NC - 1));
+      MOE_STREAM_LOAD_B(0, cb + c + 2);
       MOE_STREAM_STORE_A(1);
       MOE_BARRIER_LDS();
-      if (c + 1 >= NC) break;
-      MOE_STREAM_LOAD_A(cb + min(c + 2, NC - 1));
+      MOE_STREAM_LOAD_A(cb + c + 2);
       MOE_STREAM_COMPUTE(1);
       MOE_STREAM_LOAD_B(1, cb + min(c + 3, NC - 1));
       MOE_STREAM_STORE_A(0);
       MOE_BARRIER_LDS();
     }
+    MOE_STREAM_LOAD_A(cb + min(c + 1, NC - 1));
+    MOE_STREAM_COMPUTE(0);
+    MOE_STREAM_STORE_A(1);
+    MOE_BARRIER_LDS();
+    if (c + 1 < NC) MOE_STREAM_COMPUTE(1);
 #undef MOE_STREAM_LOAD_A
 #undef MOE_STREAM_STORE_A
 #undef MOE_STREAM_COMPUTE
