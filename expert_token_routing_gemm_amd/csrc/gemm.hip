@@ -604,12 +604,23 @@ moe_status run_ffn(const moe_ffn_args* a, const FfnPlan& pl, void* ws, hipStream
 // Split-K slices for the router GEMM on the LDS-DMA kernel (E a multiple of
 // 256: whole 256-wide tiles): enough 128-row x slice work items for two
 // workgroups per CU.
+// K slices of the router logits GEMM: enough (tile, slice) work items for
+// MOE_LOGITS_WG_PER_CU per CU, at most MOE_LOGITS_MAX_KS.  Each slice writes
+// and re-reads T x E fp32 partials, so more slices are not free: on the
+// DeepSeek-V3 share (T = 8192, E = 256) 4 slices (one item per CU) route in
+// 77 us, 8 slices (two per CU) in 85 us, 2 slices in 101 us.
+#ifndef MOE_LOGITS_WG_PER_CU
+#define MOE_LOGITS_WG_PER_CU 1
+#endif
+#ifndef MOE_LOGITS_MAX_KS
+#define MOE_LOGITS_MAX_KS 16
+#endif
 int dense_logits_ksplit(int64_t T, int d, int E) {
   if (E % 256 != 0 || d % BKE_DMA != 0) return 1;
   const int64_t m_tiles = (T + 127) / 128;
-  const int64_t target = 2 * (int64_t)device_info().cus;
+  const int64_t target = MOE_LOGITS_WG_PER_CU * (int64_t)device_info().cus;
   int ks = 1;
-  while (ks < 16 && m_tiles * ks < target && (d / BKE_DMA) % (2 * ks) == 0) ks *= 2;
+  while (ks < MOE_LOGITS_MAX_KS && m_tiles * ks < target && (d / BKE_DMA) % (2 * ks) == 0) ks *= 2;
   return ks;
 }
 
