@@ -184,6 +184,16 @@ def test_tiny_edge_shapes():
     full_parity(make_workload(3, T=300, d=128, h=256, E=64, k=1, R=16, cf=0.25), label="heavy drop")
 
 
+@pytest.mark.parametrize("T", [64, 2304])
+def test_all_256_experts_and_shared(T):
+    """The most FFN groups there can be: all 256 experts of the DeepSeek-V3
+    shape executed (fp8 weights) plus the shared expert, 257 groups; T = 64
+    takes the weight-streaming kernels, T = 2304 (18432 rows) the LDS-DMA
+    ones."""
+    full_parity(make_workload(4, T=T, d=256, h=256, e_begin=0, e_end=256),
+                label=f"E=256 all executed + shared, T={T}")
+
+
 def test_zero_capacity_drops_everything():
     """C = 0: every assignment skips its expert and every token leaves as x."""
     wl = make_workload(0, T=300, d=128, h=128)
