@@ -3,6 +3,8 @@
 #include <string.h>
 
 #include <mutex>
+#include <set>
+#include <utility>
 #include <vector>
 
 #include "common.h"
@@ -16,7 +18,7 @@ thread_local std::string g_last_error;
 void set_error(const std::string& msg) { g_last_error = msg; }
 void clear_error() { g_last_error.clear(); }
 
-const DeviceInfo& device_info() {
+DeviceInfo device_info() {
   static std::mutex mu;
   static std::vector<DeviceInfo> cache;
   static std::vector<bool> have;
@@ -39,6 +41,19 @@ const DeviceInfo& device_info() {
     have[dev] = true;
   }
   return cache[dev];
+}
+
+hipError_t set_dynamic_lds(const void* kernel, int bytes) {
+  static std::mutex mu;
+  static std::set<std::pair<int, const void*>> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.count({dev, kernel})) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.insert({dev, kernel});
+  return e;
 }
 
 moe_status expert_ffn_impl(const moe_ffn_args* a, void* ws, size_t ws_bytes, hipStream_t stream,

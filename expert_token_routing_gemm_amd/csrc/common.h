@@ -38,12 +38,16 @@ void clear_error();
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Device properties (cached per device).
+// Device properties of the current device (cached per device).
 struct DeviceInfo {
   int cus;
   int lds_bytes;
 };
-const DeviceInfo& device_info();
+DeviceInfo device_info();
+
+// Allows `kernel` `bytes` of dynamic LDS on the current device; the attribute
+// is set once per (device, kernel) and the call is thread-safe.
+hipError_t set_dynamic_lds(const void* kernel, int bytes);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 

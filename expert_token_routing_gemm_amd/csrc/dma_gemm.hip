@@ -495,12 +495,7 @@ moe_status launch_dma(const GroupedParams& p, int64_t max_routed_rows, hipStream
   constexpr size_t lds = NS * (BM * 2 + BN * (BSRC == B_FP8 ? 1 : 2)) * BKE +
                          (3 * kMaxGroups + 1 + 4) * sizeof(int);
   static_assert(per_cu * lds <= 160 * 1024, "LDS of the resident workgroups");
-  static bool attr_set = false;
-  if (!attr_set) {
-    MOE_CHECK_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                      (int)lds));
-    attr_set = true;
-  }
+  MOE_CHECK_HIP(set_dynamic_lds((const void*)kern, (int)lds));
   const int nt = p.N / BN;
   const int ngroups = p.n_routed + (p.t_dense > 0 ? 1 : 0);
   const int64_t m_tiles_ub = (max_routed_rows + BM - 1) / BM + p.n_routed +

@@ -419,12 +419,7 @@ moe_status launch(const GroupedParams& p, int64_t max_routed_rows, hipStream_t s
   constexpr int RB = MOE_BIG_RB;
   auto kern = grouped_gemm_kernel<AT, CT, BSRC, EPI, BM, BN, WM, WN, MINB, RB>;
   constexpr size_t lds = lds_bytes<BM, BN, RB>();
-  static bool attr_set = false;  // one dynamic-LDS opt-in per process
-  if (!attr_set) {
-    MOE_CHECK_HIP(hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                      (int)lds));
-    attr_set = true;
-  }
+  MOE_CHECK_HIP(set_dynamic_lds((const void*)kern, (int)lds));
   const int nt = p.N / BN;
   const int ngroups = p.n_routed + (p.t_dense > 0 ? 1 : 0);
   const int64_t m_tiles_ub = (max_routed_rows + BM - 1) / BM + p.n_routed +
