@@ -44,6 +44,7 @@ namespace {
 
 constexpr int BKE = 32;      // k elements per stage (64 bytes of bf16)
 constexpr int NSTAGE = 4;    // LDS ring depth (loads run NSTAGE-1 stages ahead)
+constexpr int kMaxFp8K = 16384;  // fp8 weights: K per GEMM (the tile's scales sit in registers)
 constexpr int kGM = 4;       // m-tiles per strip
 
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
@@ -126,6 +127,7 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
   constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   constexpr int A_BLOCKS = A_BYTES / 1024, B_BLOCKS = B_BYTES / 1024;  // 1 KB blocks per stage
   constexpr int B_ROWS_PER_BLOCK = F8 ? 32 : 16;
+  constexpr int kScRegs = F8 ? kMaxFp8K / 128 / 64 : 1;  // fp8 scale registers per B subtile
   constexpr int LPW = (A_BLOCKS + B_BLOCKS) / NW;  // DMA instructions per wave per stage
   static_assert((A_BLOCKS + B_BLOCKS) % NW == 0, "blocks split evenly over waves");
   static_assert(EPI != EPI_SWIGLU || QN % 2 == 0, "SwiGLU pairs subtiles");
@@ -189,7 +191,7 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
     bf16_t* C;
     const unsigned char* src[LPW];  // stage-0 global address of each DMA instruction
     int kstep[LPW];                 // its bytes per stage
-    const float* sp[QN];            // fp8 scale rows of the B subtiles
+    float sr[QN][kScRegs];          // fp8: scale of 128-k block 64r + lane, per B subtile
   };
   // DMA instruction i of this wave fills 1 KB block b = wave + NW*i of the
   // stage (A blocks first, then B blocks); LDS position l*16 <- lane l.
@@ -290,14 +292,20 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
 #pragma unroll
     for (int i = 0; i < LPW; ++i) c.src[i] += (int64_t)c.kbase * c.kstep[i];
     // fp8 scales: one per B subtile and 128-k block (the subtile's 32
-    // weight rows lie in one 128-row block)
+    // weight rows lie in one 128-row block), all of the tile's K range
+    // loaded here into registers (lane q of register r: block 64r + q); the
+    // main loop picks one with readlane, so it issues no vector load of its
+    // own, whose use would make the compiler wait for every LDS DMA in flight
     if constexpr (F8) {
+      const int kblocks = KT / 4;
 #pragma unroll
       for (int j = 0; j < QN; ++j) {
         const unsigned char* bm;
         const float* sm;
         const int brow = b_row(wn * WTN + j * 32, bm, sm);
-        c.sp[j] = sm + (int64_t)(brow >> 7) * p.ks;
+        const float* srow = sm + (int64_t)(brow >> 7) * p.ks + c.kbase / 4;
+#pragma unroll
+        for (int r = 0; r < kScRegs; ++r) c.sr[j][r] = srow[min(64 * r + lane, kblocks - 1)];
       }
     }
 
@@ -334,11 +342,26 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
     bf16_t* const C = cur.C;
 
     const int h = lane >> 5;  // k half of this lane: [16h, 16h + 16) of a stage
+    if constexpr (F8) {
+      // the scales have landed before the loop (one wait per tile here,
+      // instead of one in every stage)
+#pragma unroll
+      for (int j = 0; j < QN; ++j)
+#pragma unroll
+        for (int r = 0; r < kScRegs; ++r) asm volatile("" ::"v"(cur.sr[j][r]));
+    }
     for (int kt = 0; kt < KT; ++kt) {
       float sc[QN];
       if constexpr (F8) {
+        const int q = kt >> 2;  // 128-k block of this stage within the slice
 #pragma unroll
-        for (int j = 0; j < QN; ++j) sc[j] = cur.sp[j][(kbase + kt) >> 2];
+        for (int j = 0; j < QN; ++j) {
+          float v = cur.sr[j][0];
+#pragma unroll
+          for (int r = 1; r < kScRegs; ++r)
+            if (q >= 64 * r) v = cur.sr[j][r];
+          sc[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), q & 63));
+        }
       }
       wait_stage_and_barrier<LPW>(min(NS - 2, KT - 1 - kt));
       if (kt + NS - 1 < KT) issue(cur, kt + NS - 1);
@@ -511,15 +534,15 @@ moe_status launch_dma(const GroupedParams& p, int64_t max_routed_rows, hipStream
 }
 
 // Tile shapes: 256x256 with 2x4 waves of 128x64 (one workgroup per CU) for
-// large bf16 groups; 128x256 tiles of 4 waves, two workgroups per CU with a
-// 3-stage ring each, for groups of a few hundred rows (less padding, and one
-// workgroup's prologue and epilogue overlap the other's main loop) and for
-// fp8 weights (their B stage is half as large, so the second workgroup's
-// extra operand traffic costs less).  Measured: Switch workload 1.00 ->
-// 0.87 ms, DeepSeek-V3 share 1.78 -> 1.67 ms; the bf16 prefill workload stays
-// faster on 256x256 (11.8 vs 13.0 ms).  Knobs: waves along N of the 256x256
-// tile, the mean rows per group below which 128x256 tiles are used, and
-// whether fp8 weights may take 256x256 tiles (measured slower: 6-22%).
+// large groups; 128x256 tiles of 4 waves, two workgroups per CU with a
+// 3-stage ring each, for groups of a few hundred rows with no shared expert
+// (less padding, and one workgroup's prologue and epilogue overlap the
+// other's main loop).  Measured: Switch workload 1.00 -> 0.87 ms; the bf16
+// prefill workload stays faster on 256x256 (11.8 vs 13.0 ms), and so does
+// the DeepSeek-V3 share with fp8 weights (expert GEMM 1 662 -> 648 us).
+// Knobs: waves along N of the 256x256 tile, the mean rows per group below
+// which 128x256 tiles are used, and whether fp8 weights may take 256x256
+// tiles at all.
 #ifndef MOE_DMA_BIG_WN
 #define MOE_DMA_BIG_WN 4
 #endif
@@ -527,7 +550,7 @@ moe_status launch_dma(const GroupedParams& p, int64_t max_routed_rows, hipStream
 #define MOE_DMA_SMALL_ROWS 768
 #endif
 #ifndef MOE_DMA_FP8_BIG
-#define MOE_DMA_FP8_BIG 0
+#define MOE_DMA_FP8_BIG 1
 #endif
 template <int BSRC, bool TL, int EPI>
 moe_status launch_dma_shape(const GroupedParams& p, int64_t max_routed_rows, hipStream_t s) {
@@ -562,10 +585,11 @@ moe_status launch_dma_partial(const GroupedParams& p, hipStream_t stream) {
 }
 
 // bf16 or fp8 weights (row-major or tiled); output columns in whole 256-wide
-// tiles, K in whole 32-element stages (fp8: 128-element scale blocks).
+// tiles, K in whole 32-element stages (fp8: 128-element scale blocks, K at
+// most kMaxFp8K).
 bool dma_gemm_supported(const GroupedParams& p, int bsrc) {
   if (p.N % 256 != 0 || p.K % BKE != 0) return false;
-  return bsrc == B_SAME || (bsrc == B_FP8 && p.K % 128 == 0);
+  return bsrc == B_SAME || (bsrc == B_FP8 && p.K % 128 == 0 && p.K <= kMaxFp8K);
 }
 
 moe_status launch_dma_gemm(int bsrc, int epi, const GroupedParams& p, int64_t max_routed_rows,

@@ -567,7 +567,7 @@ moe_status run_ffn(const moe_ffn_args* a, const FfnPlan& pl, void* ws, hipStream
   } else if (p1.b_tiled && (sizeof(AT) == 4 || !MOE_USE_DMA_GEMM || !dma_gemm_supported(p1, BSRC) ||
                              !dma_gemm_supported(p2, BSRC))) {
     set_error("moe_expert_ffn: tiled weights need bf16 activations and, off the streaming path, "
-              "h and d multiples of 256");
+              "h and d multiples of 256 (fp8 weights: at most 16384)");
     return MOE_ERR_UNSUPPORTED;
   } else if (sizeof(AT) == 4) {
     p1.ksplit = p2.ksplit = 1;

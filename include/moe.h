@@ -199,9 +199,11 @@ moe_status moe_aux_loss(const float* logits, const int32_t* counts, int64_t T, i
  * max_rows bounds expert_off[e_end] - expert_off[e_begin] (host value; it
  * sizes the workspace and the grid; rows beyond it are a caller error).
  * w_layout applies to all six weight matrices (w1, w3, w2, ws1, ws3, ws2);
- * scales keep their layout.  MOE_W_TILED16 is supported with bf16 weights
- * and, for fp8 weights, when the streaming path runs (max_rows <= 64 per
- * executed expert and T_dense <= 64); otherwise MOE_ERR_UNSUPPORTED.
+ * scales keep their layout.  MOE_W_TILED16 needs bf16 activations (bf16 or
+ * fp8 weights).  Off the streaming path (more than 64 rows per executed
+ * expert on average, or T_dense > 64) it also needs d and h multiples of 256
+ * and, for fp8 weights, d and h at most 16384; otherwise
+ * MOE_ERR_UNSUPPORTED.  Row-major weights have no such limits.
  */
 typedef struct moe_ffn_args {
   int32_t d, h, E, e_begin, e_end;

@@ -4,9 +4,9 @@ and compare it with the fp64 oracle.
 Tolerances (max-abs error normalised by the row max, on the expert outputs
 before combine and on the layer output): fp32 1e-4, bf16 2e-2, fp8 weights
 6e-2.  Integer outputs must match bit for bit.  Route ids may differ only on
-tokens whose oracle score gap between the k-th and (k+1)-th expert is below
-1e-6; integer stages are then compared with the oracle replayed on the GPU's
-ids.
+near-ties: the selected set where the oracle's k-th and (k+1)-th scores are
+within 1e-6, the order inside it where two consecutive selected scores are;
+integer stages are then compared with the oracle replayed on the GPU's ids.
 """
 from __future__ import annotations
 
@@ -26,25 +26,47 @@ def act_to_f64(arr: np.ndarray, act_dtype: str) -> np.ndarray:
     return O.to_f64(arr, act_dtype)
 
 
+def selection_keys(wl, ref_route: dict) -> np.ndarray:
+    """fp64 keys the top-k orders by: the scores, plus the selection bias."""
+    p = ref_route["scores"]
+    return p if wl.score == "softmax" or wl.b_select is None else p + wl.b_select.astype(np.float64)
+
+
+def order_gap_of(wl, ref_route: dict) -> np.ndarray:
+    """Smallest fp64 gap between consecutive keys of the oracle's selected
+    experts (ids are listed by key, so a near-tie there only reorders them)."""
+    ids_o = ref_route["ids"]
+    if wl.k < 2:
+        return np.full(len(ids_o), np.inf)
+    chosen = np.take_along_axis(selection_keys(wl, ref_route), ids_o.astype(np.int64), axis=1)
+    return np.min(chosen[:, :-1] - chosen[:, 1:], axis=1)
+
+
 def check_route(wl, gpu: dict, ref_route: dict) -> np.ndarray:
     """ids equal except on near-ties; near-tie ids must still be a valid top-k
-    within the tie tolerance.  Returns the mask of exempt tokens."""
+    within the tie tolerance.  The selected set may differ only where the
+    k-th and (k+1)-th scores are within NEAR_TIE; the order inside the set
+    (ids are listed by score) only where two consecutive selected scores
+    are.  Returns the mask of exempt tokens."""
     ids_g, ids_o = gpu["ids"], ref_route["ids"]
     gap = ref_route["gap"]
-    exempt = gap < NEAR_TIE
+    s = selection_keys(wl, ref_route)
+    order_gap = order_gap_of(wl, ref_route)
+    set_diff = np.any(np.sort(ids_g, axis=1) != np.sort(ids_o, axis=1), axis=1)
     diff = np.any(ids_g != ids_o, axis=1)
-    bad = diff & ~exempt
+    exempt = np.minimum(gap, order_gap) < NEAR_TIE
+    bad = (set_diff & ~(gap < NEAR_TIE)) | (diff & ~exempt)
     assert not bad.any(), (f"{int(bad.sum())} tokens route differently with gap >= {NEAR_TIE}: "
-                           f"first {np.nonzero(bad)[0][:8].tolist()}, gaps {gap[bad][:8].tolist()}")
-    # exempt tokens: every chosen expert's score is within the tolerance of the k-th best
-    if diff.any():
-        p = ref_route["scores"]
-        s = p if wl.score == "softmax" or wl.b_select is None else p + wl.b_select.astype(np.float64)
-        for t in np.nonzero(diff)[0]:
-            kth = np.sort(s[t])[::-1][wl.k - 1]
-            chosen = s[t, ids_g[t]]
-            assert np.all(chosen >= kth - NEAR_TIE), f"token {t}: invalid near-tie choice"
-            assert len(set(ids_g[t].tolist())) == wl.k
+                           f"first {np.nonzero(bad)[0][:8].tolist()}, gaps {gap[bad][:8].tolist()}, "
+                           f"order gaps {order_gap[bad][:8].tolist()}")
+    # exempt tokens: every chosen expert's score is within the tolerance of
+    # the k-th best, and consecutive choices are ordered within it
+    for t in np.nonzero(diff)[0]:
+        kth = np.sort(s[t])[::-1][wl.k - 1]
+        chosen = s[t, ids_g[t]]
+        assert np.all(chosen >= kth - NEAR_TIE), f"token {t}: invalid near-tie choice"
+        assert np.all(chosen[:-1] >= chosen[1:] - NEAR_TIE), f"token {t}: ids out of order"
+        assert len(set(ids_g[t].tolist())) == wl.k
     return exempt
 
 

@@ -132,3 +132,18 @@ def test_weight_tile_rejects_bad_arguments_before_launch():
     assert L.moe_weight_tile(4096, 4096 + 512, 1, 16, 64, None) == _abi.MOE_ERR_INVALID  # overlap
     assert b"overlaps" in L.moe_last_error()
     assert L.moe_weight_tile(None, None, 0, 16, 64, None) == _abi.MOE_OK  # nothing to do
+
+
+def test_ffn_rejects_tiled_fp8_beyond_the_register_scales():
+    """Tiled fp8 weights off the streaming path keep a tile's block scales in
+    registers, which bounds d and h by 16384: beyond it, a clear error before
+    any launch (pointers are never dereferenced on this path)."""
+    fake = 1 << 20  # 16-byte aligned, never touched
+    a = _abi.FfnArgs(d=256, h=16640, E=8, e_begin=0, e_end=8, act=_abi.MOE_SWIGLU,
+                     act_dtype=_abi.MOE_BF16, w_dtype=_abi.MOE_FP8_E4M3,
+                     w_layout=_abi.MOE_W_TILED16, max_rows=8 * 1024,
+                     x_send=fake, expert_off=fake, w1=fake, w3=fake, w2=fake,
+                     s1=fake, s3=fake, s2=fake, y_send=fake)
+    need = M.lib().moe_ffn_workspace_bytes(C.byref(a))
+    assert M.lib().moe_expert_ffn(C.byref(a), fake, need, None) == _abi.MOE_ERR_UNSUPPORTED
+    assert b"tiled" in M.lib().moe_last_error()

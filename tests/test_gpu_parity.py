@@ -251,8 +251,12 @@ TILED = {
     "c4-decode": (4, dict(T=48, d=512, h=256)),
     # LDS-DMA path: bf16 and fp8 weights, 128- and 256-row tiles
     "c2-small": (2, dict(T=1000, d=512, h=640)),
+    "c2-256-row-tiles": (2, dict(T=4096, d=512, h=512)),
     "c3-small": (3, dict(T=4096, d=256, h=512)),
     "c4-small": (4, dict(T=256, d=512, h=256)),
+    # fp8 with more than 64 scale blocks along K (the second scale register)
+    "c4-long-k-gemm1": (4, dict(T=256, d=8448, h=256)),
+    "c4-long-k-gemm2": (4, dict(T=256, d=512, h=8448)),
 }
 
 
