@@ -13,7 +13,12 @@ namespace moe {
 
 namespace {
 thread_local std::string g_last_error;
+thread_local bool g_check_only = false;
 }
+
+bool check_only() { return g_check_only; }
+CheckOnly::CheckOnly() { g_check_only = true; }
+CheckOnly::~CheckOnly() { g_check_only = false; }
 
 void set_error(const std::string& msg) { g_last_error = msg; }
 void clear_error() { g_last_error.clear(); }
@@ -112,6 +117,38 @@ extern "C" moe_status moe_layer_forward(const moe_layer_args* a, void* ws, size_
     set_error("moe_layer_forward: workspace too small");
     return MOE_ERR_WORKSPACE;
   }
+  // every block's arguments and the wiring between them, before any launch
+  {
+    const CheckOnly guard;
+    moe_status st = moe_route(&a->route, ws, ws_bytes, stream);
+    if (st == MOE_OK) st = moe_dispatch(&a->dispatch, ws, ws_bytes, stream);
+    if (st == MOE_OK) st = expert_ffn_impl(&a->ffn, ws, ws_bytes, stream, nullptr);
+    if (st == MOE_OK) st = moe_combine(&a->combine, stream);
+    if (st != MOE_OK) return st;
+  }
+  clear_error();
+  const moe_route_args& r = a->route;
+  const moe_dispatch_args& ds = a->dispatch;
+  const moe_ffn_args& f = a->ffn;
+  const moe_combine_args& c = a->combine;
+  MOE_CHECK_ARG(r.T == ds.T && r.T == c.T, "route, dispatch and combine need the same T");
+  MOE_CHECK_ARG(r.k == ds.k && r.k == c.k, "route, dispatch and combine need the same k");
+  MOE_CHECK_ARG(r.E == ds.E && r.E == f.E, "route, dispatch and ffn need the same E");
+  MOE_CHECK_ARG(ds.d == f.d && ds.d == c.d && (r.x == nullptr || r.d == ds.d),
+                "all stages need the same d");
+  MOE_CHECK_ARG(r.act_dtype == ds.act_dtype && r.act_dtype == f.act_dtype &&
+                    r.act_dtype == c.act_dtype,
+                "all stages need the same act_dtype");
+  MOE_CHECK_ARG(ds.ids == r.ids && c.ids == r.ids && c.weights == r.weights && c.slot == ds.slot,
+                "ids, weights and slot must be the buffers route and dispatch write");
+  MOE_CHECK_ARG(c.e_begin == f.e_begin && c.e_end == f.e_end,
+                "ffn and combine need the same executed experts");
+  MOE_CHECK_ARG(f.e_begin == f.e_end || (f.x_send == ds.x_send && f.expert_off == ds.expert_off &&
+                                         c.y_send == f.y_send),
+                "x_send, expert_off and y_send must be wired between the stages");
+  const bool dense = f.x_dense != nullptr && f.T_dense > 0;
+  MOE_CHECK_ARG(!dense || (f.x_dense == ds.x && f.T_dense == r.T && c.shared_out == f.y_dense),
+                "the shared expert runs over the layer's x and feeds combine's shared_out");
   hipEvent_t* ev = a->events;
   if (ev && ev[0]) MOE_CHECK_HIP(hipEventRecord(ev[0], stream));
   moe_status st = moe_route(&a->route, ws, ws_bytes, stream);

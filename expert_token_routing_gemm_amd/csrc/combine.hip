@@ -180,6 +180,7 @@ extern "C" moe_status moe_combine(const moe_combine_args* a, hipStream_t stream)
                     (!a->shared_out || aligned16(a->shared_out)),
                 "rows not 16-byte aligned");
   MOE_CHECK_ARG(a->x != a->y, "y may not alias x");
+  if (check_only()) return MOE_OK;
   const int row16 = (int)((int64_t)a->d * es / 16);
   // decode-sized batches: a workgroup per token so every load is in flight at once
   const bool wide = a->T < 4 * (int64_t)device_info().cus;

@@ -38,6 +38,16 @@ void clear_error();
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Check-only mode of the calling thread: while a CheckOnly object lives,
+// every entry point validates its arguments and returns MOE_OK (or the
+// error) without launching or recording anything.  moe_layer_forward uses it
+// to check all four stages before the first launch.
+bool check_only();
+struct CheckOnly {
+  CheckOnly();
+  ~CheckOnly();
+};
+
 // Device properties of the current device (cached per device).
 struct DeviceInfo {
   int cus;

@@ -579,6 +579,7 @@ extern "C" moe_status moe_dispatch(const moe_dispatch_args* a, void* ws, size_t 
     set_error("moe_dispatch: workspace too small");
     return MOE_ERR_WORKSPACE;
   }
+  if (check_only()) return MOE_OK;
 #ifndef MOE_DISPATCH_TINY
 #define MOE_DISPATCH_TINY 1
 #endif

@@ -558,17 +558,21 @@ moe_status run_ffn(const moe_ffn_args* a, const FfnPlan& pl, void* ws, hipStream
   p2.ns = d / 128;
   p2.ksplit = pl.ks2;
 
+  const bool streaming = small_m && sizeof(AT) == 2;
+  if (!streaming && p1.b_tiled &&
+      (sizeof(AT) == 4 || !MOE_USE_DMA_GEMM || !dma_gemm_supported(p1, BSRC) ||
+       !dma_gemm_supported(p2, BSRC))) {
+    set_error("moe_expert_ffn: tiled weights need bf16 activations and, off the streaming path, "
+              "h and d multiples of 256 (fp8 weights: at most 16384)");
+    return MOE_ERR_UNSUPPORTED;
+  }
+  if (check_only()) return MOE_OK;
   moe_status st;
-  if (small_m && sizeof(AT) == 2) {
+  if (streaming) {
     st = launch_stream_gemm1_any(BSRC, a->act, p1, stream);
     if (st != MOE_OK) return st;
     if (mid_event) MOE_CHECK_HIP(hipEventRecord(mid_event, stream));
     st = launch_stream_gemm2_any(BSRC, p2, stream);
-  } else if (p1.b_tiled && (sizeof(AT) == 4 || !MOE_USE_DMA_GEMM || !dma_gemm_supported(p1, BSRC) ||
-                             !dma_gemm_supported(p2, BSRC))) {
-    set_error("moe_expert_ffn: tiled weights need bf16 activations and, off the streaming path, "
-              "h and d multiples of 256 (fp8 weights: at most 16384)");
-    return MOE_ERR_UNSUPPORTED;
   } else if (sizeof(AT) == 4) {
     p1.ksplit = p2.ksplit = 1;
     constexpr int FT = sizeof(AT) == 4 ? MOE_F32_TILE : 128;
@@ -708,6 +712,7 @@ moe_status moe::expert_ffn_impl(const moe_ffn_args* a, void* ws, size_t ws_bytes
     return MOE_ERR_WORKSPACE;
   }
   const int groups = n_routed + ((a->x_dense && a->T_dense > 0) ? 1 : 0);
+  if (groups == 0 && check_only()) return MOE_OK;
   if (groups == 0) {
     if (mid_event) MOE_CHECK_HIP(hipEventRecord(mid_event, stream));
     return MOE_OK;

@@ -639,6 +639,7 @@ extern "C" moe_status moe_route(const moe_route_args* a, void* ws, size_t ws_byt
   if (a->x == nullptr) {
     MOE_CHECK_ARG(a->logits != nullptr, "x == NULL needs input logits");
     MOE_CHECK_ARG(a->b_router == nullptr, "x == NULL: logits are final, b_router must be NULL");
+    if (check_only()) return MOE_OK;
     if (!launch_topk(a->logits, 1, a, nullptr, nullptr, grouped(a) ? a->n_groups : 0, stream)) {
       set_error("moe_route: unsupported split of the router logits");
       return MOE_ERR_INVALID;
@@ -652,6 +653,7 @@ extern "C" moe_status moe_route(const moe_route_args* a, void* ws, size_t ws_byt
   MOE_CHECK_ARG(a->d % vn == 0, "d must be a multiple of 16 bytes");
   MOE_CHECK_ARG(aligned16(a->x) && aligned16(a->w_router), "x/w_router not 16-byte aligned");
   if (small_route_fits(a)) {
+    if (check_only()) return MOE_OK;
     // Many tokens: stage W_r in LDS once per workgroup and loop over tokens.
     // Few tokens (decode): one workgroup per token, W_r read through L2.
     const bool stage = a->T > 1024;
@@ -689,6 +691,7 @@ extern "C" moe_status moe_route(const moe_route_args* a, void* ws, size_t ws_byt
     set_error("moe_route: workspace too small");
     return MOE_ERR_WORKSPACE;
   }
+  if (check_only()) return MOE_OK;
   float* raw = static_cast<float*>(ws);
   const int ks = route_ksplit(a);
   if (mfma_route(a)) {

@@ -276,8 +276,12 @@ moe_status moe_combine(const moe_combine_args* a, hipStream_t stream);
 
 /* ------------------------------------------------------------ whole layer
  * route -> dispatch -> expert FFN -> combine, enqueued on one stream with no
- * host synchronisation.  The four argument blocks must be consistent (the
- * caller wires ids, slot, x_send, ... between them).  If `events` is not
+ * host synchronisation.  The four argument blocks must be consistent: the
+ * same T, k, E, d and act_dtype, and the buffers one stage writes are the
+ * ones the next reads (ids, weights, slot, x_send, expert_off, y_send; with a
+ * shared expert, x_dense = dispatch.x, T_dense = T, shared_out = y_dense).
+ * Every block and that wiring are checked before anything is launched, so an
+ * error leaves the stream untouched.  If `events` is not
  * NULL it holds MOE_LAYER_EVENTS host-side hipEvent_t handles, recorded at
  * the stage boundaries listed at MOE_LAYER_EVENTS; a NULL entry is skipped.
  * Each recorded event delays the next kernel's start by a few microseconds,

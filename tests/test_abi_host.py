@@ -147,3 +147,46 @@ def test_ffn_rejects_tiled_fp8_beyond_the_register_scales():
     need = M.lib().moe_ffn_workspace_bytes(C.byref(a))
     assert M.lib().moe_expert_ffn(C.byref(a), fake, need, None) == _abi.MOE_ERR_UNSUPPORTED
     assert b"tiled" in M.lib().moe_last_error()
+
+
+def _layer_args():
+    """A consistent decode-sized layer (T=4, d=h=256, E=8, top-2, SwiGLU, bf16)
+    on fake 16-byte-aligned device addresses: only the checks ever see them."""
+    fk = iter(range(1 << 24, 1 << 30, 1 << 20))
+    T, d, E, k, h = 4, 256, 8, 2, 256
+    x, wr, logits, ids, wts = (next(fk) for _ in range(5))
+    counts, kept, off, rc, ro, slot, src, xs = (next(fk) for _ in range(8))
+    w1, w3, w2, ys, y = (next(fk) for _ in range(5))
+    a = _abi.LayerArgs()
+    a.route = _abi.RouteArgs(T=T, d=d, E=E, k=k, act_dtype=_abi.MOE_BF16, score=_abi.MOE_SOFTMAX,
+                             renorm=1, x=x, w_router=wr, logits=logits, ids=ids, weights=wts)
+    a.dispatch = _abi.DispatchArgs(T=T, d=d, E=E, k=k, R=1, capacity=T * k,
+                                   act_dtype=_abi.MOE_BF16, ids=ids, x=x, counts=counts, kept=kept,
+                                   expert_off=off, rank_counts=rc, rank_off=ro, slot=slot, src=src,
+                                   x_send=xs)
+    a.ffn = _abi.FfnArgs(d=d, h=h, E=E, e_begin=0, e_end=E, act=_abi.MOE_SWIGLU,
+                         act_dtype=_abi.MOE_BF16, w_dtype=_abi.MOE_BF16, max_rows=T * k,
+                         x_send=xs, expert_off=off, w1=w1, w3=w3, w2=w2, y_send=ys)
+    a.combine = _abi.CombineArgs(T=T, d=d, k=k, e_begin=0, e_end=E, act_dtype=_abi.MOE_BF16,
+                                 x=x, y_send=ys, ids=ids, slot=slot, weights=wts, y=y)
+    return a
+
+
+@pytest.mark.parametrize("breaks,match", [
+    (lambda a: setattr(a.combine, "d", 100), b"moe_combine"),          # a later stage's own check
+    (lambda a: setattr(a.combine, "k", 1), b"same k"),
+    (lambda a: setattr(a.dispatch, "T", 5), b"same T"),
+    (lambda a: setattr(a.combine, "ids", a.combine.ids + 4096), b"ids, weights and slot"),
+    (lambda a: setattr(a.ffn, "x_send", a.ffn.x_send + 4096), b"x_send, expert_off"),
+    (lambda a: setattr(a.combine, "e_end", 4), b"executed experts"),
+])
+def test_layer_checks_every_stage_and_the_wiring_before_launch(breaks, match):
+    """moe_layer_forward rejects a bad later stage or inconsistent wiring with
+    MOE_ERR_INVALID before launching anything (a launch on this GPU-less host
+    would have failed with MOE_ERR_HIP instead)."""
+    a = _layer_args()
+    breaks(a)
+    L = M.lib()
+    need = L.moe_workspace_bytes(C.byref(a))
+    assert L.moe_layer_forward(C.byref(a), 1 << 30, need, None) == _abi.MOE_ERR_INVALID
+    assert match in L.moe_last_error()
