@@ -140,6 +140,9 @@ SMALL = {
     # decode-sized batch on the streaming path with skewed routing: experts
     # of 191 and 72 rows take several 64-row passes over the same weights
     "c2-decode-skewed": (2, dict(T=256, d=256, h=384)),
+    # row-major fp8 weights with h above the LDS-DMA kernel's fp8 K limit
+    # (16384): the register-staged grouped kernel runs both expert GEMMs
+    "c4-fp8-long-h-grouped": (4, dict(T=256, d=256, h=16640)),
 }
 
 
