@@ -140,6 +140,10 @@ SMALL = {
     # decode-sized batch on the streaming path with skewed routing: experts
     # of 191 and 72 rows take several 64-row passes over the same weights
     "c2-decode-skewed": (2, dict(T=256, d=256, h=384)),
+    # GELU at the fp32 tolerance (the kernels' erf is a rational approximation)
+    # and GELU on the decode streaming path
+    "c0-gelu-fp32": (0, dict(T=600, d=256, h=256, act="gelu")),
+    "c3-decode-gelu-stream": (3, dict(T=64, d=256, h=256)),
     # row-major fp8 weights with h above the LDS-DMA kernel's fp8 K limit
     # (16384): the register-staged grouped kernel runs both expert GEMMs
     "c4-fp8-long-h-grouped": (4, dict(T=256, d=256, h=16640)),
