@@ -49,6 +49,14 @@ def _stream(stream=None) -> int:
     return s.cuda_stream
 
 
+def _used_on(stream, *tensors) -> None:
+    """Temporaries allocated on the current stream but read by work on
+    ``stream``: keep the caching allocator from reusing them before it ends."""
+    if stream is not None:
+        for t in tensors:
+            t.record_stream(stream)
+
+
 # ------------------------------------------------------------ host helpers
 
 
@@ -120,6 +128,7 @@ def moe_aux_loss(logits: torch.Tensor, counts: torch.Tensor, k: int, score: int,
     _check(lib().moe_aux_loss(_p(logits), _p(counts), int(T), int(E), int(k), int(score),
                               float(alpha), _p(pm), _p(loss), _p(ws), ws.numel(), _stream(stream)),
            "moe_aux_loss")
+    _used_on(stream, ws, pm, loss)
     return pm, loss
 
 
@@ -132,6 +141,7 @@ def moe_weight_tile(w: torch.Tensor, n_mats: int, rows: int, stream=None) -> tor
     row_bytes = nbytes // max(1, n_mats * rows)
     _check(lib().moe_weight_tile(_p(w), _p(out), int(n_mats), int(rows), int(row_bytes),
                                  _stream(stream)), "moe_weight_tile")
+    _used_on(stream, w, out)
     return out
 
 

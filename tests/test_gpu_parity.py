@@ -249,6 +249,31 @@ def test_weight_tile_layout():
         np.testing.assert_array_equal(got, want)
 
 
+def test_helpers_on_a_side_stream():
+    """moe_weight_tile (from a non-contiguous view: a temporary copy) and
+    moe_aux_loss (a temporary workspace) launched on another stream give the
+    current stream's results, with the temporaries kept alive for it."""
+    from expert_token_routing_gemm_amd import moe_aux_loss, moe_weight_tile, to_host
+    g = torch.Generator().manual_seed(9)
+    w = torch.randint(0, 256, (2, 64, 512), dtype=torch.uint8, generator=g).cuda()
+    view = w.transpose(1, 2)  # [2, 512, 64]: non-contiguous
+    logits = torch.randn((300, 64), generator=g).cuda()
+    counts = torch.randint(0, 10, (64,), dtype=torch.int32, generator=g).cuda()
+    ref_tile = to_host(moe_weight_tile(view, 2, 512))
+    ref_pm, ref_loss = (to_host(t) for t in moe_aux_loss(logits, counts, 2, 0, 0.01))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        tiled = moe_weight_tile(view, 2, 512, stream=side)
+        pm, loss = moe_aux_loss(logits, counts, 2, 0, 0.01, stream=side)
+        junk = torch.full((1 << 20,), 7, dtype=torch.uint8, device="cuda")  # reuses freed blocks
+        del junk
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_host(tiled), ref_tile)
+    np.testing.assert_array_equal(to_host(pm), ref_pm)
+    np.testing.assert_array_equal(to_host(loss), ref_loss)
+
+
 TILED = {
     # streaming path
     "c1-small": (1, dict(T=40, d=512, h=768)),
