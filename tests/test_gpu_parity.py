@@ -211,6 +211,24 @@ def test_zero_capacity_drops_everything():
     np.testing.assert_array_equal(g["y"], wl.x)
 
 
+@pytest.mark.parametrize("cfg,over", [(2, dict(T=256, d=256, h=256, e_begin=3, e_end=3)),
+                                      (4, dict(T=128, d=256, h=256, e_begin=0, e_end=0))])
+def test_rank_executing_no_experts(cfg, over):
+    """A rank whose share holds no executed expert (e_begin == e_end) still
+    routes and dispatches the full send layout; the layer output is the
+    residual bit for bit (plus the shared expert where there is one)."""
+    wl = make_workload(cfg, **over)
+    C = O.capacity(wl.T, wl.k, wl.E, wl.cf)
+    layer, g = run_layer(wl, capacity=C)
+    ref = O.layer(wl)
+    P.check_route(wl, g, ref["route"])
+    P.check_dispatch(wl, g, ref["route"]["ids"], C)
+    if wl.shared is None:
+        np.testing.assert_array_equal(g["y"], wl.x)
+    else:
+        P.check_close("y", P.act_to_f64(g["y"], wl.act_dtype), ref["y"], P.tol_of(wl))
+
+
 def test_empty_batch():
     from expert_token_routing_gemm_amd import MoELayer
     wl = make_workload(0, T=1, d=128, h=128)
