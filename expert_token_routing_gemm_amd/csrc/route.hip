@@ -616,7 +616,125 @@ __global__ void __launch_bounds__(256) topk_kernel(
   }
 }
 
+// Maximum (and sum) over the 16 lanes of each row, returned to all 16: the
+// first four steps of wave_max_u64.
+__device__ __forceinline__ uint64_t row_max_u64(uint64_t v) {
+  uint64_t o;
+  o = dpp_u64<0xb1, 0xf>(v);   v = o > v ? o : v;
+  o = dpp_u64<0x4e, 0xf>(v);   v = o > v ? o : v;
+  o = dpp_u64<0x141, 0xf>(v);  v = o > v ? o : v;
+  o = dpp_u64<0x140, 0xf>(v);  v = o > v ? o : v;
+  return v;
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_row_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row_sum_f32(float v) {
+  v += dpp_row_f32<0xb1>(v);
+  v += dpp_row_f32<0x4e>(v);
+  v += dpp_row_f32<0x141>(v);
+  v += dpp_row_f32<0x140>(v);
+  return v;
+}
+
+// Top-k for E <= 64 without group limits: four tokens per wave, one per
+// 16-lane row, each lane holding experts sub + 16 i (i < 4); the arg-max of
+// a round stays inside the row (DPP row moves, no cross-row step), and the
+// chosen expert's value comes from its lane with one bpermute.  Same
+// selection order, keys and weights as topk_kernel.
+template <int KS>
+__global__ void __launch_bounds__(256) topk_rows_kernel(
+    const float* __restrict__ logits_in, const float* __restrict__ b_router,
+    const float* __restrict__ b_select, float* __restrict__ logits_out, int32_t* __restrict__ ids,
+    float* __restrict__ weights, int64_t T_tok, int E, int k, int score, int renorm) {
+  constexpr int PER = 4, RL = 16;  // experts per lane, lanes per row
+  const int lane = lane_id();
+  const int sub = lane & (RL - 1), row0 = lane & ~(RL - 1);
+  const int64_t rows_total = (int64_t)gridDim.x * (blockDim.x / RL);
+  // the 16 lanes of a row share t, so a row runs or leaves the loop whole
+  // and the row moves only ever read active lanes
+  for (int64_t t = (int64_t)blockIdx.x * (blockDim.x / RL) + threadIdx.x / RL; t < T_tok;
+       t += rows_total) {
+    float part[PER][KS];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int ec = min(sub + i * RL, E - 1);
+#pragma unroll
+      for (int z = 0; z < KS; ++z) part[i][z] = logits_in[(int64_t)z * T_tok * E + t * E + ec];
+    }
+    float L[PER], sc[PER];
+    uint64_t pk[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = sub + i * RL;
+      float l = part[i][0];
+#pragma unroll
+      for (int z = 1; z < KS; ++z) l += part[i][z];
+      L[i] = l + ((b_router && e < E) ? b_router[e] : 0.f);
+      if (logits_out && e < E) logits_out[t * E + e] = L[i];
+      float key;
+      if (score == MOE_SIGMOID) {
+        sc[i] = sigmoid_f32_via_f64(L[i]);
+        key = (b_select && e < E) ? sc[i] + b_select[e] : sc[i];
+      } else {
+        sc[i] = 0.f;
+        key = L[i];
+      }
+      pk[i] = e < E ? ((uint64_t)key_image(key) << 32) | (uint32_t)(0xffffffffu - (uint32_t)e) : 0ull;
+    }
+    int sel_e = -1;
+    float sel_v = 0.f, first_logit = 0.f;
+    for (int j = 0; j < k; ++j) {
+      uint64_t mine = 0;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) mine = pk[i] > mine ? pk[i] : mine;
+      const uint64_t win = row_max_u64(mine);
+      const int bi = (int)(0xffffffffu - (uint32_t)win);  // uniform within the row
+      const int owner = bi & (RL - 1), slot = bi / RL;
+      float v = 0.f;
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (i == slot) {
+          v = (score == MOE_SIGMOID) ? sc[i] : L[i];
+          if (sub == owner) pk[i] = 0;
+        }
+      const float bv = __shfl(v, row0 + owner, kWave);
+      if (sub == j) {
+        sel_e = bi;
+        sel_v = bv;
+      }
+      if (j == 0) first_logit = bv;
+    }
+    float num, denom;
+    if (score == MOE_SOFTMAX) {
+      num = (sub < k) ? __expf(sel_v - first_logit) : 0.f;
+      if (renorm) {
+        denom = num;
+      } else {
+        denom = 0.f;
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+          if (sub + i * RL < E) denom += __expf(L[i] - first_logit);
+      }
+    } else {
+      num = (sub < k) ? sel_v : 0.f;
+      denom = num;
+    }
+    denom = row_sum_f32(denom);
+    if (score == MOE_SIGMOID && !renorm) denom = 1.f;
+    if (sub < k) {
+      ids[t * k + sub] = sel_e;
+      weights[t * k + sub] = num / denom;
+    }
+  }
+}
+
 int grid_for(int64_t units, int per_block);
+
+#ifndef MOE_TOPK_ROWS
+#define MOE_TOPK_ROWS 1
+#endif
 
 template <int PERN>
 bool launch_topk_p(const float* in, int ks, const moe_route_args* a, const float* b_router,
@@ -646,6 +764,25 @@ bool launch_topk_p(const float* in, int ks, const moe_route_args* a, const float
 // ks is a power of two <= 16.
 bool launch_topk(const float* in, int ks, const moe_route_args* a, const float* b_router,
                  float* logits_out, int ng, hipStream_t stream) {
+  if (MOE_TOPK_ROWS && a->E <= 64 && (ng == 0 || a->topk_groups >= ng)) {
+    const dim3 grid(grid_for(a->T, 16)), tb(256);
+    switch (ks) {
+#define MOE_TOPK_ROWS_CASE(K_)                                                                 \
+  case K_:                                                                                   \
+    topk_rows_kernel<K_><<<grid, tb, 0, stream>>>(in, b_router, a->b_select, logits_out, a->ids, \
+                                                  a->weights, a->T, a->E, a->k, a->score,   \
+                                                  a->renorm);                               \
+    return true;
+      MOE_TOPK_ROWS_CASE(1)
+      MOE_TOPK_ROWS_CASE(2)
+      MOE_TOPK_ROWS_CASE(4)
+      MOE_TOPK_ROWS_CASE(8)
+      MOE_TOPK_ROWS_CASE(16)
+#undef MOE_TOPK_ROWS_CASE
+      default:
+        return false;
+    }
+  }
   const int pern = (a->E + kWave - 1) / kWave;
   if (pern <= 1) return launch_topk_p<1>(in, ks, a, b_router, logits_out, ng, stream);
   if (pern <= 2) return launch_topk_p<2>(in, ks, a, b_router, logits_out, ng, stream);
