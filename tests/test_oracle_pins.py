@@ -502,8 +502,86 @@ def test_group_limited_route_weights_and_gap(c4_small):
     r = O.route(x64, wr64, None, wl.b_select, wl.k, "sigmoid", True, n_groups=8, topk_groups=4)
     assert all(len(set((r["ids"][t] // 32).tolist())) <= 4 for t in range(wl.T))
     np.testing.assert_allclose(r["weights"].sum(axis=1), 1.0, rtol=1e-14)
-    plain = O.route(x64, wr64, None, wl.b_select, wl.k, "sigmoid", True)
-    assert np.all(r["gap"] <= np.maximum(plain["gap"], r["gap"]))
+    # the near-tie gap never exceeds the group-score gap
+    s64 = O.sigmoid(r["logits"]) + wl.b_select.astype(np.float64)
+    assert np.all(r["gap"] <= O.group_gap(s64, 8, 4))
+
+
+def _sig(v):
+    return 1.0 / (1.0 + math.exp(-v))
+
+
+def test_group_gap_hand_values():
+    """group_gap = (topk_groups-th best group score) - (next one), a group's
+    score being its largest expert score.  Catches: a group scored by its sum
+    or mean instead of its max, the wrong pair of ranks, a sign error."""
+    s = np.array([[0.10, 0.90, 0.50, 0.60],     # groups {0,1} {2,3}: maxes 0.90, 0.60
+                  [0.20, 0.30, 0.35, 0.10]])    # maxes 0.30, 0.35 -> sorted 0.35, 0.30
+    np.testing.assert_allclose(O.group_gap(s, 2, 1), [0.30, 0.05], rtol=0, atol=1e-15)
+    s3 = np.array([[0.10, 0.70, 0.65, 0.20, 0.30, 0.40]])  # maxes 0.70, 0.65, 0.40
+    np.testing.assert_allclose(O.group_gap(s3, 3, 2), [0.25], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(O.group_gap(s3, 3, 1), [0.05], rtol=0, atol=1e-15)
+    # every group kept: no group boundary, infinite gap
+    assert np.isinf(O.group_gap(s3, 3, 3)).all()
+
+
+def test_group_limited_route_gap_hand_values():
+    """route()'s near-tie gap with groups = min(group gap, gap between the
+    k-th and (k+1)-th expert inside the kept groups), on sigmoid scores
+    computed here with math.exp.  Row 0: the group gap decides; row 1: the
+    expert gap inside the kept group decides.  Catches either term dropped."""
+    L = np.array([[0.0, 2.0, 1.0, 1.5],
+                  [1.0, 1.125, -3.0, -2.0]], np.float32)  # exact in fp32
+    r = O.route(None, None, None, None, 1, "sigmoid", True, logits32=L, n_groups=2,
+                topk_groups=1)
+    g0 = _sig(2.0) - _sig(1.5)          # group maxes sigma(2) vs sigma(1.5)
+    e0 = _sig(2.0) - _sig(0.0)          # inside group 0: sigma(2) vs sigma(0)
+    g1 = _sig(1.125) - _sig(-2.0)
+    e1 = _sig(1.125) - _sig(1.0)
+    np.testing.assert_allclose(r["gap"], [min(g0, e0), min(g1, e1)], rtol=0, atol=1e-15)
+    assert min(g0, e0) == g0 and min(g1, e1) == e1
+    np.testing.assert_array_equal(r["ids"][:, 0], [1, 1])
+
+
+def test_sigmoid_key_adds_bias_after_sigmoid():
+    """The selection key is sigma(L) + b, not sigma(L + b) (the bias is added
+    to the router scores: Ultralytics, "Load Balancing and Capacity",
+    bias-based balancing bullet).  With L = [0, 3], b = [0.5, 0]:
+    sigma(0) + 0.5 = 1.0 beats sigma(3) = 0.9526, so expert 0 is chosen,
+    while sigma(L + b) = [0.622, 0.953] would choose expert 1.  The weight
+    uses the unbiased score: sigma(0) = 0.5 without renormalisation."""
+    L = np.array([[0.0, 3.0]], np.float32)
+    b = np.array([0.5, 0.0], np.float32)
+    key = O.selection_keys32(L, "sigmoid", b)
+    np.testing.assert_array_equal(key, np.array([[np.float32(0.5) + np.float32(0.5),
+                                                  np.float32(_sig(3.0))]], np.float32))
+    r = O.route(None, None, None, b, 1, "sigmoid", False, logits32=L)
+    assert r["ids"][0, 0] == 0
+    np.testing.assert_allclose(r["weights"][0, 0], 0.5, rtol=0, atol=1e-15)
+    # the fp64 near-tie gap is taken on sigma + b as well: 1.0 - 0.9526
+    np.testing.assert_allclose(r["gap"][0], 1.0 - _sig(3.0), rtol=0, atol=1e-12)
+    # the opposite composition would pick expert 1
+    assert _sig(0.0 + 0.5) < _sig(3.0)
+
+
+def test_rowmax_rel_err_hand_values():
+    """The tolerance metric: max over rows of (max_i |got - ref|) / (max_i
+    |ref|).  Hand values where the plausible variants differ: normalising by
+    the global max gives 0.01, averaging over rows 0.055, normalising by
+    |got| 0.0909; the stated metric gives 0.1."""
+    ref = np.array([[1.0, 0.5], [100.0, 0.0]])
+    got = np.array([[1.1, 0.5], [100.0, 1.0]])
+    assert O.rowmax_rel_err(got, ref) == pytest.approx(0.1, abs=1e-15)
+    # sign of the error does not matter
+    assert O.rowmax_rel_err(2 * ref - got, ref) == pytest.approx(0.1, abs=1e-15)
+    # a negative reference entry sets the row's scale through its magnitude
+    assert O.rowmax_rel_err(np.array([[-3.0, 0.3]]), np.array([[-4.0, 0.0]])) == \
+        pytest.approx(0.25, abs=1e-15)
+    # an all-zero reference row falls back to the absolute error
+    assert O.rowmax_rel_err(np.array([[0.5, 0.0]]), np.zeros((1, 2))) == 0.5
+    # identical arrays and empty arrays give zero
+    assert O.rowmax_rel_err(ref, ref) == 0.0
+    assert O.rowmax_rel_err(np.zeros((0, 3)), np.zeros((0, 3))) == 0.0
 
 
 # ---------------------------------------------------------------- bias balancing
