@@ -2,13 +2,17 @@
 
 One step = one moe_layer_forward (route -> dispatch -> expert FFN -> combine)
 over one batch of seeded synthetic input, inputs resident in HBM.  Default
-workload: the decode-shaped Mixtral-style bf16 layer (T=128 tokens, d=4096,
-8 SwiGLU experts with h=14336, top-2, softmax renormalised, no drops).
+workload: the prefill-shaped Mixtral-style bf16 layer (T=16384 tokens,
+d=4096, 8 SwiGLU experts with h=14336, top-2, softmax renormalised, skewed
+logit offsets, no drops), the largest of the five workloads by flops and
+bytes; ``--config i`` selects another.
 
-Prints one JSON line: tokens/s over the timed steps, per-stage times from HIP
-events recorded between the kernels inside the timed region, the roofline of
-the dominant kernel (the first expert GEMM, which streams w1 and w3) and the
-fp64 CPU oracle timed on the host on a bounded sample of the same workload.
+Prints one JSON line: tokens/s over the timed steps (back to back), the
+roofline of the dominant kernel (the first expert GEMM) from HIP events
+recorded around it on the stream it runs on, per-stage times from further
+steps with an event at every stage boundary and the 256 MB Infinity Cache
+flushed before each of them, and the fp64 CPU oracle timed on the host on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -27,10 +31,13 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3       # dense fp32 matrix
-# sources whose code the decode GEMM1 counters in profiles/ were taken on
-TRAFFIC_SOURCES = ("expert_token_routing_gemm_amd/csrc/stream_gemm.hip",
-                   "expert_token_routing_gemm_amd/csrc/gemm_common.h",
-                   "expert_token_routing_gemm_amd/csrc/common.h")
+FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA
+# rocprofv3 FETCH_SIZE/WRITE_SIZE records of each workload's first expert
+# GEMM (per launch, calibrated against a plain copy); each is reported only
+# while the sources it lists hash to its recorded value
+TRAFFIC_RECORDS = {1: "profiles/gemm1_decode_traffic.json",
+                   2: "profiles/gemm1_prefill_traffic.json"}
+MALL_FLUSH_MIB = 512           # > 2x the 256 MB Infinity Cache
 STAGES = ["route", "dispatch", "gemm1", "gemm2", "combine"]
 
 
@@ -94,43 +101,72 @@ def gemm_flops(wl, kept_rows: int, shared: bool):
     return {"gemm1": 2 * n1 * wl.d * wl.h * nx, "gemm2": 2 * wl.d * wl.h * nx}
 
 
-def sources_sha256() -> str:
+def sources_sha256(files) -> str:
     h = hashlib.sha256()
-    for f in TRAFFIC_SOURCES:
+    for f in files:
         h.update(open(os.path.join(ROOT, f), "rb").read())
     return h.hexdigest()
 
 
-def traffic_from_profiles(w_layout: str):
-    """HBM bytes per launch of the decode workload's first expert GEMM from
+def traffic_from_profiles(cfg: int, w_layout: str):
+    """HBM bytes per launch of the workload's first expert GEMM from
     committed rocprofv3 counter runs, valid only while the kernel sources
     and the weight layout are the ones the counters were taken on."""
-    path = os.path.join(ROOT, "profiles", "gemm1_decode_traffic.json")
-    if not os.path.exists(path):
+    name = TRAFFIC_RECORDS.get(cfg)
+    path = os.path.join(ROOT, name) if name else None
+    if not path or not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("source_sha256") != sources_sha256() or rec.get("w_layout") != w_layout:
+    if rec.get("source_sha256") != sources_sha256(rec.get("sources", [])) or \
+            rec.get("w_layout") != w_layout:
         return None
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, budget_s: float = 10.0, max_reps: int = 8):
-    """The fp64 oracle on the host cores: whole-layer forwards of the same
-    workload, repeated until about budget_s seconds of CPU work (at most
-    max_reps); the rate is tokens over the total time."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def token_sample(wl, n: int):
+    """The workload restricted to its first n tokens (same weights, router
+    and offsets): the bounded sample the CPU oracle is timed on."""
+    if n >= wl.T:
+        return wl
+    sub = types.SimpleNamespace(**vars(wl))
+    sub.T = n
+    sub.x = wl.x[:n]
+    return sub
+
+
+def cpu_baseline(wl, budget_s: float = 12.0, max_reps: int = 8, max_tokens: int = 2048):
+    """The fp64 oracle on the host cores: whole-layer forwards of the
+    workload's first ``max_tokens`` tokens (all of them for smaller
+    workloads), repeated until about budget_s seconds of CPU work (at most
+    max_reps); the rate is tokens over the total time.  Every forward decodes
+    the expert weights to fp64 again, as the oracle does."""
     import threadpoolctl
 
     from oracle import oracle as O
     threads = max((p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()
                    if p.get("user_api") == "blas"), default=1)
+    sub = token_sample(wl, max_tokens)
     reps, dt = 0, 0.0
     while reps < max_reps and (reps == 0 or dt < budget_s):
         t0 = time.perf_counter()
-        O.layer(wl)
+        O.layer(sub)
         dt += time.perf_counter() - t0
         reps += 1
-    return {"value": reps * wl.T / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{reps} x the whole layer on all {wl.T} tokens of the same workload, fp64, "
+    what = (f"all {wl.T} tokens" if sub.T == wl.T else
+            f"the first {sub.T} of the {wl.T} tokens (same weights and routing rule)")
+    return {"value": reps * sub.T / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"{reps} x the whole layer on {what} of the same workload, fp64, "
                       f"{dt:.1f} s in total (input generation excluded)"}
 
 
@@ -233,7 +269,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=1, help="workload index 0-4 (default 1: decode)")
+    ap.add_argument("--config", type=int, default=2,
+                    help="workload index 0-4 (default 2: the prefill-shaped Mixtral layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--w-layout", choices=["rowmajor", "tiled"], default=None,
                     help="expert weight layout (default: tiled, re-laid out once at load time, "
@@ -297,14 +334,21 @@ def main():
     ms_per_step = wall * 1e3 / K
     value = wl.T * K / wall
 
-    # Stage breakdown, after the timed region: all stage-boundary events
-    # (these steps run slower by the events' own gaps).
+    # Stage breakdown, after the timed region: an event at every stage
+    # boundary, and before each such step a 512 MiB write that evicts the
+    # layer's buffers from the 256 MB Infinity Cache (outside the events), so
+    # every stage starts cache-cold as in a model where other layers run in
+    # between.
     KB = min(K, 20)
+    flush = torch.empty((MALL_FLUSH_MIB << 20,), dtype=torch.uint8, device="cuda:0")
     ev = Events(hip, n * KB)
     for s in range(KB):
+        flush.fill_(s & 0xFF)
         layer.forward(events=ev.ev[s * n:(s + 1) * n])
     torch.cuda.synchronize()
+    del flush
     per = {st: [] for st in STAGES}
+    step_cold = []
     for s in range(KB):
         b = s * n
         per["route"].append(ev.ms(b + 0, b + 1))
@@ -312,7 +356,8 @@ def main():
         per["gemm1"].append(ev.ms(b + 2, b + 3))
         per["gemm2"].append(ev.ms(b + 3, b + 4))
         per["combine"].append(ev.ms(b + 4, b + 5))
-    step_with_events_ms = ev.ms(0, (KB - 1) * n + n - 1) / KB
+        step_cold.append(ev.ms(b + 0, b + 5))
+    step_cold_ms = float(np.mean(step_cold))
     ev.close()
     stage_ms = {k: float(np.mean(v)) for k, v in per.items()}
 
@@ -331,15 +376,18 @@ def main():
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS}
         roof["kernel"] = "stream_gemm_kernel (expert GEMM 1: w1/w3 + SwiGLU, weight streaming)"
-        roof["traffic"] = traffic_from_profiles(w_layout)
     else:
+        # the MFMA instructions the kernel issues are bf16 (fp8 weights are
+        # widened to bf16 in registers) or fp32: that dtype's peak
         peak = FP32_PEAK_TFLOPS if wl.act_dtype == "f32" else BF16_PEAK_TFLOPS
         achieved = flops["gemm1"] / g1_s / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                 "frac": achieved / peak}
         roof["kernel"] = ("grouped_gemm_kernel (fp32 MFMA" if wl.act_dtype == "f32"
                           else "dma_gemm_kernel (bf16 MFMA") + ", expert GEMM 1 + activation)"
-        roof["traffic"] = None
+        if wl.w_dtype == "fp8":
+            roof["frac_of_fp8_peak"] = achieved / FP8_PEAK_TFLOPS
+    roof["traffic"] = traffic_from_profiles(args.config, w_layout)
     roof["algorithmic_bytes"] = nbytes["gemm1"]
     roof["algorithmic_flops"] = flops["gemm1"]
     stage_frac = {st: (nbytes[st] / (stage_ms[st] / 1e3) / 1e9) / HBM_PEAK_GBS for st in STAGES}
@@ -366,7 +414,9 @@ def main():
         "gemm1_ms_timed": gemm1_ms,
         "stages_ms": stage_ms,
         "stages_note": (f"stage times from {KB} further steps with an event at every stage "
-                        f"boundary ({step_with_events_ms:.4f} ms per step with those events)"),
+                        f"boundary, each after a {MALL_FLUSH_MIB} MiB write that flushes the "
+                        f"Infinity Cache ({step_cold_ms:.4f} ms per such step)"),
+        "ms_per_step_cache_cold": step_cold_ms,
         "stages_hbm_frac": stage_frac,
         "gemm_tflops": {k: flops[k] / (stage_ms[k] / 1e3) / 1e12 for k in flops},
         "kept_rows": kept_rows,
