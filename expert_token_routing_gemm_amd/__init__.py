@@ -20,7 +20,7 @@ import torch
 
 from . import _abi
 from ._abi import (INT32_MAX, MOE_BF16, MOE_F32, MOE_FP8_E4M3, MOE_GELU, MOE_LAYER_EVENTS,  # noqa: F401
-                   MOE_RELU, MOE_SIGMOID, MOE_SOFTMAX, MOE_SWIGLU, MOE_W_ROWMAJOR, MOE_W_TILED16,
+                   MOE_STATIC_SCRATCH_BYTES, MOE_RELU, MOE_SIGMOID, MOE_SOFTMAX, MOE_SWIGLU, MOE_W_ROWMAJOR, MOE_W_TILED16,
                    CombineArgs, DispatchArgs,
                    FfnArgs, LayerArgs, RouteArgs, lib)
 
@@ -149,6 +149,12 @@ def moe_layer_forward(a: LayerArgs, workspace: Optional[torch.Tensor], stream=No
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().moe_layer_forward(C.byref(a), _p(workspace), ws_bytes, _stream(stream)),
            "moe_layer_forward")
+
+
+def moe_layer_forward_noalloc(a: LayerArgs, stream=None) -> None:
+    """The layer forward on the library's static scratch (no workspace)."""
+    _check(lib().moe_layer_forward_noalloc(C.byref(a), _stream(stream)),
+           "moe_layer_forward_noalloc")
 
 
 # ------------------------------------------------------------ buffers
@@ -310,13 +316,22 @@ class MoELayer:
         """Whole layer; ``events`` = list of MOE_LAYER_EVENTS raw hipEvent_t
         handles (ints; None skips that boundary) recorded at the stage
         boundaries, or None."""
+        self._set_events(events)
+        moe_layer_forward(self.args, self.workspace, stream)
+
+    def _set_events(self, events):
         if events is not None:
             arr = (C.c_void_p * MOE_LAYER_EVENTS)(*events)
             self.args.events = C.cast(arr, C.POINTER(C.c_void_p))
             self._ev_keep = arr
         else:
             self.args.events = None
-        moe_layer_forward(self.args, self.workspace, stream)
+
+    def forward_noalloc(self, events=None, stream=None):
+        """Whole layer through the no-allocation entry point (the library's
+        static scratch instead of this layer's workspace)."""
+        self._set_events(events)
+        moe_layer_forward_noalloc(self.args, stream)
 
     def results(self) -> dict:
         torch.cuda.synchronize(self.device)

@@ -20,6 +20,7 @@ MOE_W_ROWMAJOR, MOE_W_TILED16 = 0, 1
 MOE_MAX_EXPERTS = 256
 MOE_MAX_TOPK = 8
 MOE_LAYER_EVENTS = 6
+MOE_STATIC_SCRATCH_BYTES = 64 << 20
 INT32_MAX = 2 ** 31 - 1
 
 vp = C.c_void_p
@@ -81,6 +82,7 @@ PROTOTYPES = {
     "moe_combine": (C.c_int, [C.POINTER(CombineArgs), vp]),
     "moe_workspace_bytes": (C.c_size_t, [C.POINTER(LayerArgs)]),
     "moe_layer_forward": (C.c_int, [C.POINTER(LayerArgs), vp, C.c_size_t, vp]),
+    "moe_layer_forward_noalloc": (C.c_int, [C.POINTER(LayerArgs), vp]),
     "moe_last_error": (C.c_char_p, []),
 }
 

@@ -300,6 +300,21 @@ size_t moe_workspace_bytes(const moe_layer_args* a);
 moe_status moe_layer_forward(const moe_layer_args* a, void* workspace, size_t ws_bytes,
                              hipStream_t stream);
 
+/* ------------------------------------------------- no-allocation variant
+ * For callers that cannot allocate device memory or hand over a workspace
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The same layer forward as moe_layer_forward, same arguments,
+ * results and errors, with the workspace taken from a static device array
+ * inside the library: MOE_STATIC_SCRATCH_BYTES on every GPU the library runs
+ * on, held until the process ends.  The caller still owns and passes every
+ * input and output.  A layer whose moe_workspace_bytes() exceeds the array
+ * returns MOE_ERR_WORKSPACE before anything is launched.  The call allocates
+ * and frees nothing.  All calls on one GPU share that GPU's array; nothing in
+ * it has to start at zero, but calls that overlap on one GPU (on different
+ * streams, or from threads without ordering between them) race on it. */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_layer_forward_noalloc(const moe_layer_args* a, hipStream_t stream);
+
 /* Message for the calling thread's most recent non-OK status ("" if none). */
 const char* moe_last_error(void);
 
