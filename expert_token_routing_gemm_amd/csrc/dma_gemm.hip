@@ -7,17 +7,26 @@
 // Design (MI355X-specific):
 //  * 256x256 output tile per workgroup of 8 waves (2 per SIMD); each wave
 //    owns 128x64 as 4x2 v_mfma_f32_32x32x16_bf16 subtiles (the full-rate bf16
-//    MFMA on gfx950; 128 fp32 accumulators per lane).  Per k the workgroup
-//    reads 8*(128+64)*2 bytes of LDS and writes 512*2 by DMA for 2*256*256
-//    flops, about 0.03 B/flop: within LDS bandwidth at the MFMA peak, where
-//    64x64 wave tiles are not.  Groups of a few hundred rows and fp8 weights
-//    use 128x256 tiles (4 waves of 128x64), two workgroups per CU.
-//  * Global -> LDS with global_load_lds_dwordx4 (no register staging): a
-//    ring of 32-k stages (4 stages of 32 KB for 256x256, 3 of 24 KB for
-//    128x256), filled NS-1 stages ahead;
-//    each wave waits for its own loads of a stage (vmcnt), then one
-//    workgroup barrier makes them visible.  The compiler does not track
-//    these waits, they are issued explicitly.
+//    MFMA on gfx950; 128 fp32 accumulators per lane).  Groups averaging a few
+//    hundred rows (with no shared expert) use 128x256 tiles of 4 waves, two
+//    workgroups per CU.
+//  * Global -> LDS with global_load_lds_dwordx4 (no register staging) into
+//    a ring of 32-k stages: 4 stages of 32 KB (24 KB with fp8 weights) for
+//    256x256 tiles, 3 for 128x256.  Each wave waits for its own loads of a
+//    stage (vmcnt), then a workgroup barrier makes them visible; the
+//    compiler does not track these waits, they are issued explicitly.
+//  * 256x256 main loop: one barrier per stage, between its two 16-k steps.
+//    The MFMAs of one step run while the fragments of the next step are
+//    read from LDS, so no MFMA waits on an LDS read issued just before it
+//    (with both waves of a SIMD waiting on their reads at once, the matrix
+//    core idled; LDS reads themselves overlap MFMAs fully when nothing waits
+//    on them).  What still costs time is the LDS-DMA writes contending with
+//    the fragment reads: measured on this chip, DMA, fragment reads and
+//    MFMAs at this kernel's ratio (4 KB DMA, 12 KB of reads and 16 MFMAs per
+//    wave) sustain ~70% of the MFMA rate, half the DMA per MFMA ~96%.
+//  * 128x256 main loop (and the split-K router GEMM): one barrier at the
+//    top of each stage, the stage's fragments read, then its MFMAs; two
+//    workgroups per CU overlap one another's waits.
 //  * Every wave instruction fills 1 KB of LDS.  Row-major 16-bit operands:
 //    16 tile rows x 64 bytes, four consecutive lanes per row (full 64-byte
 //    global segments); inside the block the 16-byte chunks of row r are
@@ -43,7 +52,7 @@ namespace moe {
 namespace {
 
 constexpr int BKE = 32;      // k elements per stage (64 bytes of bf16)
-constexpr int NSTAGE = 4;    // LDS ring depth (loads run NSTAGE-1 stages ahead)
+constexpr int NSTAGE = 4;    // LDS ring depth of the 256x256 tiles
 constexpr int kMaxFp8K = 16384;  // fp8 weights: K per GEMM (the tile's scales sit in registers)
 constexpr int kGM = 4;       // m-tiles per strip
 
@@ -74,6 +83,23 @@ __device__ __forceinline__ void wait_stage_and_barrier(int ahead) {
   if (ahead >= 2) {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * LPW) : "memory");
   } else if (ahead == 1) {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LPW) : "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+}
+
+// Waits until at most `stages` later stages of this wave's DMA (LPW
+// instructions each, 0 <= stages <= 3) are in flight and its LDS reads have
+// returned, then synchronises the workgroup.
+template <int LPW>
+__device__ __forceinline__ void wait_dma_and_barrier(int stages) {
+  static_assert(3 * LPW <= 63, "vmcnt range");
+  if (stages >= 3) {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(3 * LPW) : "memory");
+  } else if (stages == 2) {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * LPW) : "memory");
+  } else if (stages == 1) {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LPW) : "memory");
   } else {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -114,11 +140,11 @@ template <int BSRC, bool TL, int EPI, int BM, int BN, int WM_, int WN_, int NS, 
           bool PART>
 __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedParams p) {
   constexpr bool F8 = BSRC == B_FP8;
-  // bf16 256x256 tiles read a stage's fragments up front (measured on the
-  // prefill expert GEMMs: 2-3% faster; the 128x256 tiles, two workgroups per
-  // CU, are not faster that way and keep reads interleaved with the MFMAs)
-  constexpr bool kHoist = !F8 && BM == 256 && BKE == 32;
   constexpr int NW = WM_ * WN_;                  // waves
+  // 8-wave 256x256 tiles: one barrier per stage, in the middle (see below)
+  constexpr bool kMB = NW == 8 && BM == 256 && !PART;
+  // stages of DMA issued before a tile's main loop
+  constexpr int kPre = kMB ? NS : NS - 1;
   constexpr int kThreads = 64 * NW;
   constexpr int WTM = BM / WM_, WTN = BN / WN_;  // wave tile
   constexpr int QM = WTM / 32, QN = WTN / 32;    // 32x32 subtiles per wave
@@ -327,7 +353,7 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
     // every wave has finished reading the tile table's neighbours; ring free
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-    for (int s = 0; s < NS - 1; ++s)
+    for (int s = 0; s < kPre; ++s)
       if (s < KT) issue(cur, s);
   }
   for (int work = first; work < W; work += G) {
@@ -350,6 +376,121 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
 #pragma unroll
         for (int r = 0; r < kScRegs; ++r) asm volatile("" ::"v"(cur.sr[j][r]));
     }
+    if constexpr (kMB) {
+      // Two waves per SIMD, 128x64 per wave, one workgroup barrier per
+      // stage placed between the stage's two 16-k steps.  The MFMAs of one
+      // step run while the fragments of the next step are read from LDS, so
+      // no MFMA waits for an LDS read issued just before it:
+      //   step 0 of stage kt: MFMAs on X (step 0 of kt) | read Y = step 1 of kt
+      //   barrier: every wave's DMA of stage kt + 1 has landed and its reads
+      //            of stage kt have returned, so stage kt + 1 is visible and
+      //            the slot of stage kt is free
+      //   DMA of stage kt + NS into the slot of stage kt
+      //   step 1 of stage kt: MFMAs on Y | read X = step 0 of kt + 1
+      // fp8 weights: a lane's 16 B fragment bytes hold both steps of a stage,
+      // read with step 0 and converted to bf16 after the step-1 MFMAs.
+      u32x4 aX[QM], aY[QM], bX[QN], bY[QN];
+      uint32_t raw[QN][4];
+      auto rd_a = [&](int kt, int step, u32x4 (&aq)[QM]) {
+        const unsigned char* st = ring + (kt % NS) * STAGE_BYTES;
+        const int c = 2 * h + step;  // A chunk: k [16h + 8 step, +8)
+#pragma unroll
+        for (int i = 0; i < QM; ++i) {
+          const int R = wm * WTM + i * 32 + (lane & 31), r = R & 15;
+          aq[i] = *reinterpret_cast<const u32x4*>(st + (R >> 4) * 1024 + (r * 4 + (c ^ swz(r))) * 16);
+        }
+      };
+      auto rd_b = [&](int kt, int step, u32x4 (&bq)[QN]) {
+        const unsigned char* st = ring + (kt % NS) * STAGE_BYTES;
+#pragma unroll
+        for (int j = 0; j < QN; ++j) {
+          const int R = wn * WTN + j * 32 + (lane & 31), r = R & 15;
+          if constexpr (F8) {
+            const int boff = TL ? ((R >> 4) & 1) * 512 + (16 * h + r) * 16 : (R & 31) * 32 + h * 16;
+            const u32x4 w8 = *reinterpret_cast<const u32x4*>(st + A_BYTES + (R >> 5) * 1024 + boff);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) raw[j][q] = w8[q];
+          } else {
+            const int c = 2 * h + step;
+            const int boff = TL ? (16 * c + r) * 16 : (r * 4 + (c ^ swz(r))) * 16;
+            bq[j] = *reinterpret_cast<const u32x4*>(st + A_BYTES + (R >> 4) * 1024 + boff);
+          }
+        }
+      };
+      // fp8: raw bytes of stage kt -> bf16 B fragments of both steps
+      auto cvt_b = [&](int kt) {
+        if constexpr (F8) {
+          const int q = kt >> 2;  // 128-k block of the stage within the slice
+#pragma unroll
+          for (int j = 0; j < QN; ++j) {
+            float v = cur.sr[j][0];
+#pragma unroll
+            for (int r = 1; r < kScRegs; ++r)
+              if (q >= 64 * r) v = cur.sr[j][r];
+            const float sc =
+                __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), q & 63));
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+              u32x4 o;
+#pragma unroll
+              for (int wv = 0; wv < 2; ++wv) {
+                const uint32_t word = raw[j][2 * s2 + wv];
+                typedef float f2_t __attribute__((ext_vector_type(2)));
+                const f2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
+                const f2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
+                o[2 * wv] = bf16_pair(lo.x * sc, lo.y * sc);
+                o[2 * wv + 1] = bf16_pair(hi.x * sc, hi.y * sc);
+              }
+              if (s2 == 0) bX[j] = o;
+              else bY[j] = o;
+            }
+          }
+        }
+      };
+      auto mma = [&](const u32x4 (&aq)[QM], const u32x4 (&bq)[QN]) {
+#pragma unroll
+        for (int i = 0; i < QM; ++i)
+#pragma unroll
+          for (int j = 0; j < QN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8_t, aq[i]), __builtin_bit_cast(bf16x8_t, bq[j]), acc[i][j],
+                0, 0, 0);
+      };
+      wait_dma_and_barrier<LPW>(min(NS - 1, KT - 1));  // stage 0 visible
+      rd_a(0, 0, aX);
+      rd_b(0, 0, bX);
+      if constexpr (F8) cvt_b(0);
+      for (int kt = 0; kt < KT; ++kt) {
+        // step 0 of stage kt; read step 1
+        rd_a(kt, 1, aY);
+        if constexpr (!F8) rd_b(kt, 1, bY);
+        mma(aX, bX);
+        constexpr int kR1 = F8 ? QM : QM + QN;
+#pragma unroll
+        for (int r = 0; r < kR1; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, QM * QN - kR1, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_dma_and_barrier<LPW>(min(NS - 2, KT - 2 - kt));
+        if (kt + NS < KT) issue(cur, kt + NS);
+        // step 1 of stage kt; read step 0 of stage kt + 1 (at the last stage
+        // a slot whose contents are not used)
+        rd_a(kt + 1, 0, aX);
+        rd_b(kt + 1, 0, bX);
+        mma(aY, bY);
+        constexpr int kR2 = QM + QN;
+#pragma unroll
+        for (int r = 0; r < kR2; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, QM * QN - kR2, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (F8) cvt_b(kt + 1);
+      }
+    } else
     for (int kt = 0; kt < KT; ++kt) {
       float sc[QN];
       if constexpr (F8) {
@@ -366,42 +507,7 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
       wait_stage_and_barrier<LPW>(min(NS - 2, KT - 1 - kt));
       if (kt + NS - 1 < KT) issue(cur, kt + NS - 1);
       const unsigned char* st = ring + (kt % NS) * STAGE_BYTES;
-      if constexpr (kHoist) {
-        // every fragment of the stage is read up front, step by step, and the
-        // scheduler issues step 0's reads, one MFMA (which waits for them),
-        // step 1's reads, then the other MFMAs: one LDS round trip per stage
-        // is exposed instead of one per A fragment
-        u32x4 bq[QN][2], aq[2][QM];
-#pragma unroll
-        for (int step = 0; step < 2; ++step) {
-          const int c = 2 * h + step;
-#pragma unroll
-          for (int j = 0; j < QN; ++j) {
-            const int R = wn * WTN + j * 32 + (lane & 31), r = R & 15;
-            const int boff = TL ? (16 * c + r) * 16 : (r * 4 + (c ^ swz(r))) * 16;
-            bq[j][step] = *reinterpret_cast<const u32x4*>(st + A_BYTES + (R >> 4) * 1024 + boff);
-          }
-#pragma unroll
-          for (int i = 0; i < QM; ++i) {
-            const int R = wm * WTM + i * 32 + (lane & 31), r = R & 15;
-            aq[step][i] =
-                *reinterpret_cast<const u32x4*>(st + (R >> 4) * 1024 + (r * 4 + (c ^ swz(r))) * 16);
-          }
-        }
-#pragma unroll
-        for (int step = 0; step < 2; ++step)
-#pragma unroll
-          for (int i = 0; i < QM; ++i)
-#pragma unroll
-            for (int j = 0; j < QN; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  __builtin_bit_cast(bf16x8_t, aq[step][i]),
-                  __builtin_bit_cast(bf16x8_t, bq[j][step]), acc[i][j], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, QN + QM, 0);  // LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);        // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, QN + QM, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * QM * QN - 1, 0);
-      } else {
+      {
         u32x4 bq[QN][2];  // B fragments of both k-steps
 #pragma unroll
         for (int j = 0; j < QN; ++j) {
@@ -457,23 +563,29 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
     if (more) {
       setup(work + G, nxt);
 #pragma unroll
-      for (int s = 0; s < NS - 1; ++s)
+      for (int s = 0; s < kPre; ++s)
         if (s < KT) issue(nxt, s);
     }
+    // The epilogue's addresses are formed from copies that an empty asm
+    // statement hides from the compiler: otherwise it computes the 64-bit row
+    // addresses before the main loop and keeps them live through it.
+    int e_rows = rows, e_m0 = m0, e_nt = n_t, e_z = z, e_g = g;
+    bf16_t* e_C = C;
+    asm volatile("" : "+v"(e_rows), "+v"(e_m0), "+v"(e_nt), "+v"(e_z), "+v"(e_g), "+v"(e_C));
     // epilogue: value v of a lane is row 8*(v/4) + 4*(lane/32) + v%4,
     // column lane%32 of its 32x32 subtile
     if constexpr (PART) {
       const int64_t prow0 =
-          dense ? p.max_rows : (int64_t)(s_r0[g] - (p.n_routed > 0 ? p.off[p.e_begin] : 0));
+          dense ? p.max_rows : (int64_t)(s_r0[e_g] - (p.n_routed > 0 ? p.off[p.e_begin] : 0));
 #pragma unroll
       for (int i = 0; i < QM; ++i) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int row = m0 + wm * WTM + i * 32 + 8 * (v / 4) + 4 * (lane >> 5) + (v % 4);
-          if (row >= rows) continue;
-          float* prow = p.partial + ((int64_t)z * p.prow_total + prow0 + row) * p.ldc;
+          const int row = e_m0 + wm * WTM + i * 32 + 8 * (v / 4) + 4 * (lane >> 5) + (v % 4);
+          if (row >= e_rows) continue;
+          float* prow = p.partial + ((int64_t)e_z * p.prow_total + prow0 + row) * p.ldc;
 #pragma unroll
-          for (int j = 0; j < QN; ++j) prow[n_t * BN + wn * WTN + j * 32 + (lane & 31)] = acc[i][j][v];
+          for (int j = 0; j < QN; ++j) prow[e_nt * BN + wn * WTN + j * 32 + (lane & 31)] = acc[i][j][v];
         }
       }
     } else {
@@ -481,19 +593,19 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
       for (int i = 0; i < QM; ++i) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int row = m0 + wm * WTM + i * 32 + 8 * (v / 4) + 4 * (lane >> 5) + (v % 4);
-          if (row >= rows) continue;
-          bf16_t* crow = C + (int64_t)row * p.ldc;
+          const int row = e_m0 + wm * WTM + i * 32 + 8 * (v / 4) + 4 * (lane >> 5) + (v % 4);
+          if (row >= e_rows) continue;
+          bf16_t* crow = e_C + (int64_t)row * p.ldc;
           if (EPI == EPI_SWIGLU) {
 #pragma unroll
             for (int j = 0; j < QN / 2; ++j) {
-              const int col = n_t * (BN / 2) + wn * (WTN / 2) + j * 32 + (lane & 31);
+              const int col = e_nt * (BN / 2) + wn * (WTN / 2) + j * 32 + (lane & 31);
               store_c<true>(crow + col, act_silu(acc[i][j][v]) * acc[i][j + QN / 2][v]);
             }
           } else {
 #pragma unroll
             for (int j = 0; j < QN; ++j) {
-              const int col = n_t * BN + wn * WTN + j * 32 + (lane & 31);
+              const int col = e_nt * BN + wn * WTN + j * 32 + (lane & 31);
               float x = acc[i][j][v];
               if (EPI == EPI_RELU) x = fmaxf(x, 0.f);
               if (EPI == EPI_GELU) x = act_gelu(x);
@@ -540,25 +652,14 @@ moe_status launch_dma(const GroupedParams& p, int64_t max_routed_rows, hipStream
 // other's main loop).  Measured: Switch workload 1.00 -> 0.87 ms; the bf16
 // prefill workload stays faster on 256x256 (11.8 vs 13.0 ms), and so does
 // the DeepSeek-V3 share with fp8 weights (expert GEMM 1 662 -> 648 us).
-// Knobs: waves along N of the 256x256 tile, the mean rows per group below
-// which 128x256 tiles are used, and whether fp8 weights may take 256x256
-// tiles at all.
-#ifndef MOE_DMA_BIG_WN
-#define MOE_DMA_BIG_WN 4
-#endif
-#ifndef MOE_DMA_SMALL_ROWS
-#define MOE_DMA_SMALL_ROWS 768
-#endif
-#ifndef MOE_DMA_FP8_BIG
-#define MOE_DMA_FP8_BIG 1
-#endif
+// Groups average fewer than kSmallRows rows -> 128x256 tiles.
+constexpr int64_t kSmallRows = 768;
 template <int BSRC, bool TL, int EPI>
 moe_status launch_dma_shape(const GroupedParams& p, int64_t max_routed_rows, hipStream_t s) {
   const int groups = p.n_routed > 0 ? p.n_routed : 1;
-  const bool small_tiles = (BSRC == B_FP8 && !MOE_DMA_FP8_BIG) ||
-                           (p.t_dense == 0 && max_routed_rows / groups < MOE_DMA_SMALL_ROWS);
+  const bool small_tiles = p.t_dense == 0 && max_routed_rows / groups < kSmallRows;
   if (small_tiles) return launch_dma<BSRC, TL, EPI, 128, 256, 1, 4, 3, 2>(p, max_routed_rows, s);
-  return launch_dma<BSRC, TL, EPI, 256, 256, 2, MOE_DMA_BIG_WN>(p, max_routed_rows, s);
+  return launch_dma<BSRC, TL, EPI, 256, 256, 2, 4>(p, max_routed_rows, s);
 }
 
 template <int BSRC, bool TL>
