@@ -2,8 +2,8 @@
 // auxiliary balancing loss value.
 //
 // Both serve the aim the pages state in Ultralytics "Expert Parallelism",
-// "Load Balancing and Capacity": a layer finishes only when its busiest GPU
-// does.  Bias balancing: the selection bias of overloaded experts goes down
+// "Load Balancing and Capacity": the most loaded GPU sets the time of the
+// whole layer.  Bias balancing: the selection bias of overloaded experts goes down
 // and of idle ones up after each step.  Auxiliary loss: an extra loss term
 // rewards spreading tokens evenly (its form is not on the pages; the
 // Switch-Transformer form alpha * E * sum_e f_e * P_e is used).

@@ -1,10 +1,12 @@
 // Combine: un-permute, router-weighted sum and residual (gfx950).
 //
-// The expert outputs return to the token's origin, are weighted by the
-// router scores and summed (Ultralytics glossary "Expert Parallelism", "How
-// Tokens Move Between GPUs", step 4); a skipped token continues through the
-// residual connection unchanged ("Load Balancing and Capacity", paragraph
-// after the bullets; ai360xpert "Load Balancing and Dropped Tokens").
+// Each token's expert outputs come back to where the token started; each is
+// scaled by the token's router weight for that expert and the results are
+// added (Ultralytics glossary "Expert Parallelism", "How Tokens Move Between
+// GPUs", step 4).  A token that lost its expert slots to the capacity limit
+// leaves the layer as its residual input, untouched ("Load Balancing and
+// Capacity", paragraph after the bullets; ai360xpert "Load Balancing and
+// Dropped Tokens").
 //
 // One wave per token, 128-bit loads and stores over the row.  The sum is
 // accumulated in fp32 starting from x (and the shared-expert output), adding

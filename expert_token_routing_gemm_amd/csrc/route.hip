@@ -1,8 +1,8 @@
 // Route: router logits, scores and top-k (gfx950).
 //
 // Ultralytics glossary "Expert Parallelism", "How Tokens Move Between GPUs",
-// step 1: the router is a linear layer that scores every token against every
-// expert and keeps the top k.  The score function, weight renormalisation and
+// step 1: a linear layer produces one score per (token, expert) pair and
+// each token goes to its k highest-scoring experts.  The score function, weight renormalisation and
 // tie order are not on the pages: softmax or sigmoid, optional
 // renormalisation over the selected experts, ties to the lower expert index.
 // The selection-only bias follows "Load Balancing and Capacity" (bias-based

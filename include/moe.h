@@ -63,8 +63,8 @@ typedef enum { MOE_W_ROWMAJOR = 0, MOE_W_TILED16 = 1 } moe_w_layout;
 
 /* ------------------------------------------------------------------ route
  * Router scores and top-k (Ultralytics, "How Tokens Move Between GPUs",
- * step 1: a linear router scores every token against every expert and keeps
- * the top k).  logits = x W_r^T + b_router, in fp32.
+ * step 1: a linear layer gives each token one score per expert, and each
+ * token goes to its k highest-scoring experts).  logits = x W_r^T + b_router, in fp32.
  *   score = MOE_SOFTMAX: probabilities p = softmax(logits) over all E; the
  *           selection key is the logit itself (same order as p).
  *   score = MOE_SIGMOID: p = sigmoid(logits); the selection key is

@@ -34,7 +34,8 @@ Where it comes from (page titles and sections of the source pages):
   balancing bullet).
 * Token order is preserved through dispatch, compute and combine
   (mbrenndoerfer "Summary", implementation bullet on variable-length buffers).
-* Combine: outputs are weighted by the router scores and summed at the origin
+* Combine: at the token's origin each expert output is scaled by its router
+  weight and the scaled outputs are added
   (Ultralytics, "How Tokens Move Between GPUs", step 4).
 
 Readings where the pages are silent (score function, renormalisation, FFN
@@ -171,7 +172,7 @@ def topk_select(key: np.ndarray, k: int) -> np.ndarray:
 def group_limit_keys(key32: np.ndarray, n_groups: int, topk_groups: int) -> np.ndarray:
     """Group-limited routing: each token may use experts of at most
     ``topk_groups`` of the ``n_groups`` contiguous expert groups (DeepSeek-V3
-    sends each token to experts on at most 4 nodes: Ultralytics, "Load
+    lets one token use experts of no more than four nodes: Ultralytics, "Load
     Balancing and Capacity", communication paragraph).  How the groups are
     chosen is not on the pages; reading taken: a group's score is its largest
     selection key, the best ``topk_groups`` groups are kept (score desc, group
