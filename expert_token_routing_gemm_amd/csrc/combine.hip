@@ -22,15 +22,8 @@ constexpr int kThreads = 256;
 
 // The layer output is written once and not read back here: nontemporal
 // stores (measured: Switch combine 44 -> 41 us, DeepSeek-V3 share 75 -> 70 us).
-#ifndef MOE_COMBINE_NT
-#define MOE_COMBINE_NT 1
-#endif
 __device__ __forceinline__ void store_y(uint4* dst, const uint4& v) {
-  if constexpr (MOE_COMBINE_NT) {
-    __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(dst));
-  } else {
-    *dst = v;
-  }
+  __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(dst));
 }
 
 template <typename T>

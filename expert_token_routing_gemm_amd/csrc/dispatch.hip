@@ -35,12 +35,8 @@ constexpr int kWaves = kThreads / 64;
 // Send-buffer rows are written once and not read again by this kernel's
 // workgroups: nontemporal stores (measured: prefill dispatch 86 -> 76 us,
 // DeepSeek-V3-share dispatch 220 -> 209 us).
-#ifndef MOE_PACK_NT
-#define MOE_PACK_NT 1
-#endif
 __device__ __forceinline__ void store_row16(u32x4* dst, u32x4 v) {
-  if constexpr (MOE_PACK_NT) __builtin_nontemporal_store(v, dst);
-  else *dst = v;
+  __builtin_nontemporal_store(v, dst);
 }
 
 __global__ void __launch_bounds__(kThreads) hist_kernel(const int32_t* __restrict__ ids,
@@ -251,10 +247,7 @@ constexpr int kSmallThreads = 1024;
 constexpr int kSmallWaves = kSmallThreads / 64;
 // Largest assignment count for this path (measured: the tiny workload's 8192
 // assignments take 19 us on the multi-block path against 27 us here).
-#ifndef MOE_SMALL_ASSIGN
-#define MOE_SMALL_ASSIGN 4096
-#endif
-constexpr int kSmallAssign = MOE_SMALL_ASSIGN;
+constexpr int kSmallAssign = 4096;
 
 __global__ void __launch_bounds__(kSmallThreads) plan_small_kernel(
     const int32_t* __restrict__ ids, int64_t n_assign, int k, int E, int R, int C,
@@ -537,16 +530,12 @@ struct Plan {
 // busy.  Measured with one block per CU: DeepSeek-V3 share (top-8) dispatch
 // 212 -> 204 us, Switch (top-1) 36 -> 50 us, top-2 workloads within 1 us;
 // so one block per CU from top-4 up.
-#ifndef MOE_DISPATCH_BLOCKS_PER_CU
-#define MOE_DISPATCH_BLOCKS_PER_CU 2
-#endif
-#ifndef MOE_DISPATCH_BLOCKS_PER_CU_WIDE
-#define MOE_DISPATCH_BLOCKS_PER_CU_WIDE 1
-#endif
+constexpr int kDispatchBlocksPerCu = 2;
+constexpr int kDispatchBlocksPerCuWide = 1;
 Plan plan_for(int64_t T, int k) {
   int tb = kThreads / k;  // TB*k <= 256
   const int64_t target_blocks =
-      (k >= 4 ? MOE_DISPATCH_BLOCKS_PER_CU_WIDE : MOE_DISPATCH_BLOCKS_PER_CU) *
+      (k >= 4 ? kDispatchBlocksPerCuWide : kDispatchBlocksPerCu) *
       (int64_t)device_info().cus;
   const int64_t small = (T + target_blocks - 1) / target_blocks;
   if (small < tb) tb = (int)(small < 1 ? 1 : small);
@@ -598,10 +587,7 @@ extern "C" moe_status moe_dispatch(const moe_dispatch_args* a, void* ws, size_t 
     return MOE_ERR_WORKSPACE;
   }
   if (check_only()) return MOE_OK;
-#ifndef MOE_DISPATCH_TINY
-#define MOE_DISPATCH_TINY 1
-#endif
-  if (MOE_DISPATCH_TINY && a->T > 0 && a->T * a->k <= kTinyAssign) {
+  if (a->T > 0 && a->T * a->k <= kTinyAssign) {
     plan_pack_tiny_kernel<<<(int)a->T, kThreads, 0, stream>>>(
         a->ids, a->T, a->k, a->E, a->R, a->capacity, a->counts, a->kept, a->expert_off,
         a->rank_counts, a->rank_off, a->slot, a->src, (const u32x4*)a->x, (u32x4*)a->x_send, row16);

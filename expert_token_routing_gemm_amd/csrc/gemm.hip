@@ -36,15 +36,8 @@
 #include "gemm.h"
 #include "gemm_common.h"
 
-// Many-row bf16 groups use the LDS-DMA 256x256 kernel when shapes allow.
-#ifndef MOE_USE_DMA_GEMM
-#define MOE_USE_DMA_GEMM 1
-#endif
-
 // Padding (bytes) after each LDS tile row of the LDS-staged kernel.
-#ifndef MOE_LDS_PAD
-#define MOE_LDS_PAD 16
-#endif
+constexpr int kLdsPad = 16;
 
 namespace moe {
 namespace {
@@ -83,7 +76,7 @@ __global__ void __launch_bounds__(kThreads, MINB) grouped_gemm_kernel(GroupedPar
   // RB: bytes of a tile row per K-stage (128 or 64); LDS rows are padded by
   // 16 bytes so the 16 lanes reading one MFMA fragment hit distinct banks.
   constexpr int kRowBytes = RB;
-  constexpr int kLdsRow = RB + MOE_LDS_PAD;
+  constexpr int kLdsRow = RB + kLdsPad;
   constexpr int CPR = RB / 16;               // 16-byte chunks per row
   constexpr int RPP = kThreads / CPR;        // rows covered by one pass of the block
   constexpr int STEPS = RB / 64;             // MFMA k-steps per stage
@@ -392,31 +385,23 @@ __global__ void __launch_bounds__(kThreads, MINB) grouped_gemm_kernel(GroupedPar
 
 // Tile of the LDS-staged grouped GEMM for many-row groups (bf16 MFMA):
 // BM x BN with 2 x 2 waves, MINB workgroups per CU.
-#ifndef MOE_BIG_BM
-#define MOE_BIG_BM 128
-#endif
-#ifndef MOE_BIG_BN
-#define MOE_BIG_BN 128
-#endif
-#ifndef MOE_BIG_MINB
-#define MOE_BIG_MINB 2
-#endif
+constexpr int kBigBm = 128;
+constexpr int kBigBn = 128;
+constexpr int kBigMinb = 2;
 
 template <int BM, int BN, int RB>
 constexpr size_t lds_bytes() {
-  return 2 * (BM + BN) * (RB + MOE_LDS_PAD) + (3 * kMaxGroups + 1 + 4) * sizeof(int);
+  return 2 * (BM + BN) * (RB + kLdsPad) + (3 * kMaxGroups + 1 + 4) * sizeof(int);
 }
 
 struct LaunchCfg {
   int grid;
 };
 
-#ifndef MOE_BIG_RB
-#define MOE_BIG_RB 64
-#endif
+constexpr int kBigRb = 64;
 template <typename AT, typename CT, int BSRC, int EPI, int BM, int BN, int WM, int WN, int MINB>
 moe_status launch(const GroupedParams& p, int64_t max_routed_rows, hipStream_t stream) {
-  constexpr int RB = MOE_BIG_RB;
+  constexpr int RB = kBigRb;
   auto kern = grouped_gemm_kernel<AT, CT, BSRC, EPI, BM, BN, WM, WN, MINB, RB>;
   constexpr size_t lds = lds_bytes<BM, BN, RB>();
   MOE_CHECK_HIP(set_dynamic_lds((const void*)kern, (int)lds));
@@ -486,12 +471,8 @@ FfnPlan plan_ffn(const moe_ffn_args* a) {
 // kernel.  64x64 tiles, four workgroups per CU (measured on the tiny fp32
 // workload, 8192 rows x 512 x 512 per GEMM: 74 -> 56 us per GEMM against
 // 128x128 tiles; 64x64 with two per CU: 62 us).
-#ifndef MOE_F32_TILE
-#define MOE_F32_TILE 64
-#endif
-#ifndef MOE_F32_MINB
-#define MOE_F32_MINB 4
-#endif
+constexpr int kF32Tile = 64;
+constexpr int kF32Minb = 4;
 template <typename AT, int BSRC>
 moe_status run_ffn(const moe_ffn_args* a, const FfnPlan& pl, void* ws, hipStream_t stream,
                    hipEvent_t mid_event) {
@@ -560,7 +541,7 @@ moe_status run_ffn(const moe_ffn_args* a, const FfnPlan& pl, void* ws, hipStream
 
   const bool streaming = small_m && sizeof(AT) == 2;
   if (!streaming && p1.b_tiled &&
-      (sizeof(AT) == 4 || !MOE_USE_DMA_GEMM || !dma_gemm_supported(p1, BSRC) ||
+      (sizeof(AT) == 4 || !dma_gemm_supported(p1, BSRC) ||
        !dma_gemm_supported(p2, BSRC))) {
     set_error("moe_expert_ffn: tiled weights need bf16 activations and, off the streaming path, "
               "h and d multiples of 256 (fp8 weights: at most 16384)");
@@ -575,13 +556,13 @@ moe_status run_ffn(const moe_ffn_args* a, const FfnPlan& pl, void* ws, hipStream
     st = launch_stream_gemm2_any(BSRC, p2, stream);
   } else if (sizeof(AT) == 4) {
     p1.ksplit = p2.ksplit = 1;
-    constexpr int FT = sizeof(AT) == 4 ? MOE_F32_TILE : 128;
-    constexpr int FB = FT == 128 ? 2 : MOE_F32_MINB;
+    constexpr int FT = sizeof(AT) == 4 ? kF32Tile : 128;
+    constexpr int FB = FT == 128 ? 2 : kF32Minb;
     st = launch_gemm1<AT, BSRC, FT, FT, 2, 2, FB>(a->act, p1, rows, stream);
     if (st != MOE_OK) return st;
     if (mid_event) MOE_CHECK_HIP(hipEventRecord(mid_event, stream));
     st = launch<AT, AT, BSRC, EPI_NONE, FT, FT, 2, 2, FB>(p2, rows, stream);
-  } else if (MOE_USE_DMA_GEMM && dma_gemm_supported(p1, BSRC) && dma_gemm_supported(p2, BSRC)) {
+  } else if (dma_gemm_supported(p1, BSRC) && dma_gemm_supported(p2, BSRC)) {
     p1.ksplit = p2.ksplit = 1;
     const int epi1 = a->act == MOE_RELU ? EPI_RELU : (a->act == MOE_GELU ? EPI_GELU : EPI_SWIGLU);
     st = launch_dma_gemm(BSRC, epi1, p1, rows, stream);
@@ -590,10 +571,10 @@ moe_status run_ffn(const moe_ffn_args* a, const FfnPlan& pl, void* ws, hipStream
     st = launch_dma_gemm(BSRC, EPI_NONE, p2, rows, stream);
   } else {
     p1.ksplit = p2.ksplit = 1;
-    st = launch_gemm1<AT, BSRC, MOE_BIG_BM, MOE_BIG_BN, 2, 2, MOE_BIG_MINB>(a->act, p1, rows, stream);
+    st = launch_gemm1<AT, BSRC, kBigBm, kBigBn, 2, 2, kBigMinb>(a->act, p1, rows, stream);
     if (st != MOE_OK) return st;
     if (mid_event) MOE_CHECK_HIP(hipEventRecord(mid_event, stream));
-    st = launch<AT, AT, BSRC, EPI_NONE, MOE_BIG_BM, MOE_BIG_BN, 2, 2, MOE_BIG_MINB>(p2, rows, stream);
+    st = launch<AT, AT, BSRC, EPI_NONE, kBigBm, kBigBn, 2, 2, kBigMinb>(p2, rows, stream);
   }
   return st;
 }
@@ -604,22 +585,18 @@ moe_status run_ffn(const moe_ffn_args* a, const FfnPlan& pl, void* ws, hipStream
 // 256: whole 256-wide tiles): enough 128-row x slice work items for two
 // workgroups per CU.
 // K slices of the router logits GEMM: enough (tile, slice) work items for
-// MOE_LOGITS_WG_PER_CU per CU, at most MOE_LOGITS_MAX_KS.  Each slice writes
+// kLogitsWgPerCu per CU, at most kLogitsMaxKs.  Each slice writes
 // and re-reads T x E fp32 partials, so more slices are not free: on the
 // DeepSeek-V3 share (T = 8192, E = 256) 4 slices (one item per CU) route in
 // 77 us, 8 slices (two per CU) in 85 us, 2 slices in 101 us.
-#ifndef MOE_LOGITS_WG_PER_CU
-#define MOE_LOGITS_WG_PER_CU 1
-#endif
-#ifndef MOE_LOGITS_MAX_KS
-#define MOE_LOGITS_MAX_KS 16
-#endif
+constexpr int kLogitsWgPerCu = 1;
+constexpr int kLogitsMaxKs = 16;
 int dense_logits_ksplit(int64_t T, int d, int E) {
   if (E % 256 != 0 || d % BKE_DMA != 0) return 1;
   const int64_t m_tiles = (T + 127) / 128;
-  const int64_t target = MOE_LOGITS_WG_PER_CU * (int64_t)device_info().cus;
+  const int64_t target = kLogitsWgPerCu * (int64_t)device_info().cus;
   int ks = 1;
-  while (ks < MOE_LOGITS_MAX_KS && m_tiles * ks < target && (d / BKE_DMA) % (2 * ks) == 0) ks *= 2;
+  while (ks < kLogitsMaxKs && m_tiles * ks < target && (d / BKE_DMA) % (2 * ks) == 0) ks *= 2;
   return ks;
 }
 

@@ -69,12 +69,9 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// Top-k selection rounds reduce the packed keys with DPP (1) or with three
-// shuffles per butterfly step (0).  Measured: DeepSeek-V3 share route
-// 76 -> 68 us, Switch 38 -> 35.5 us.
-#ifndef MOE_TOPK_DPP
-#define MOE_TOPK_DPP 1
-#endif
+// Top-k selection rounds reduce packed (key, index) values with DPP row
+// moves (measured against three shuffles per butterfly step: DeepSeek-V3
+// share route 76 -> 68 us, Switch 38 -> 35.5 us).
 
 // fp32 of sigmoid evaluated in double: the selection key precision.
 __device__ __forceinline__ float sigmoid_f32_via_f64(float x) {
@@ -189,9 +186,7 @@ __device__ void finish_token_small(const float* L, int E, int k, int score, int 
 }
 
 // ---------------------------------------------------------------- E <= 8 fused
-#ifndef MOE_RS_TPW
-#define MOE_RS_TPW 4  // tokens per wave in flight
-#endif
+constexpr int kRsTpw = 4;  // tokens per wave in flight
 // Block = 4 waves; each wave owns TPW tokens at a time.  Lane l covers the
 // 16-byte chunks l, l+64, ... of a row (coalesced 128-bit loads of x).
 template <typename T, int TPW, bool WR_LDS>
@@ -522,7 +517,6 @@ __global__ void __launch_bounds__(256) topk_kernel(
     int sel_e = -1;      // lane j < k keeps the j-th selection
     float sel_v = 0.f;   // its logit (softmax) or sigmoid score
     float first_logit = 0.f;
-#if MOE_TOPK_DPP
     // (key, index) packed so that one unsigned max picks the larger key and,
     // on equal keys, the lower expert index; 0 marks a taken expert
     uint64_t pk[PER];
@@ -553,41 +547,6 @@ __global__ void __launch_bounds__(256) topk_kernel(
       }
       if (j == 0) first_logit = bv;
     }
-#else
-    for (int j = 0; j < k; ++j) {
-      float bk = -INFINITY;
-      int bi = 0x7fffffff;
-      float bv = 0.f;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const int e = lane + i * kWave;
-        if (!taken[i] && key_better(key[i], e, bk, bi)) {
-          bk = key[i];
-          bi = e;
-          bv = (score == MOE_SIGMOID) ? sc[i] : L[i];
-        }
-      }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ok = __shfl_xor(bk, off, kWave);
-        const int oi = __shfl_xor(bi, off, kWave);
-        const float ov = __shfl_xor(bv, off, kWave);
-        if (key_better(ok, oi, bk, bi)) {
-          bk = ok;
-          bi = oi;
-          bv = ov;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < PER; ++i)
-        if (lane + i * kWave == bi) taken[i] = true;
-      if (lane == j) {
-        sel_e = bi;
-        sel_v = bv;
-      }
-      if (j == 0) first_logit = bv;
-    }
-#endif
     // weights
     float num = 0.f;
     float denom;
@@ -732,9 +691,6 @@ __global__ void __launch_bounds__(256) topk_rows_kernel(
 
 int grid_for(int64_t units, int per_block);
 
-#ifndef MOE_TOPK_ROWS
-#define MOE_TOPK_ROWS 1
-#endif
 
 template <int PERN>
 bool launch_topk_p(const float* in, int ks, const moe_route_args* a, const float* b_router,
@@ -764,7 +720,7 @@ bool launch_topk_p(const float* in, int ks, const moe_route_args* a, const float
 // ks is a power of two <= 16.
 bool launch_topk(const float* in, int ks, const moe_route_args* a, const float* b_router,
                  float* logits_out, int ng, hipStream_t stream) {
-  if (MOE_TOPK_ROWS && a->E <= 64 && (ng == 0 || a->topk_groups >= ng)) {
+  if (a->E <= 64 && (ng == 0 || a->topk_groups >= ng)) {
     const dim3 grid(grid_for(a->T, 16)), tb(256);
     switch (ks) {
 #define MOE_TOPK_ROWS_CASE(K_)                                                                 \
@@ -870,7 +826,7 @@ extern "C" moe_status moe_route(const moe_route_args* a, void* ws, size_t ws_byt
     const bool stage = a->T > 1024;
     const size_t lds = stage ? (size_t)a->E * a->d * (a->act_dtype == MOE_F32 ? 4 : 2) : 0;
     if (stage) {
-      constexpr int TPW = MOE_RS_TPW;
+      constexpr int TPW = kRsTpw;
       const int grid = (int)std::min<int64_t>((a->T + 4 * TPW - 1) / (4 * TPW),
                                               (int64_t)device_info().cus * 2);
       if (a->act_dtype == MOE_F32) {

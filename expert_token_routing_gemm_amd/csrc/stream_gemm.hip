@@ -13,12 +13,8 @@ constexpr int kThreads = kGemmThreads;
 // Waves per workgroup of the streaming kernel (they share one A staging).
 // The SwiGLU GEMM may use another count that divides its output columns
 // into whole rounds of resident workgroups (see stream_waves).
-#ifndef MOE_SG_WAVES
-#define MOE_SG_WAVES 8
-#endif
-#ifndef MOE_SG_WAVES_ALT
-#define MOE_SG_WAVES_ALT 7
-#endif
+constexpr int kSgWaves = 8;
+constexpr int kSgWavesAlt = 7;
 
 // ---------------------------------------------------------------- weight streaming
 // Decode-sized groups (at most a few tens of rows per expert) are bound by
@@ -34,36 +30,21 @@ constexpr int kThreads = kGemmThreads;
 // Tuning of the weight-streaming kernel: K chunk and minimum waves per SIMD
 // for the SwiGLU pair and for single-matrix GEMMs, and whether row subtiles
 // past a group's rows are skipped (branches) or computed on padding rows.
-#ifndef MOE_SG_CK
-#define MOE_SG_CK 64
-#endif
-#ifndef MOE_SG_MINW
-#define MOE_SG_MINW 4
-#endif
-#ifndef MOE_SG_SKIP
-#define MOE_SG_SKIP 1
-#endif
-#ifndef MOE_DN_CK
-#define MOE_DN_CK 64
-#endif
-#ifndef MOE_DN_MINW
-#define MOE_DN_MINW 4
-#endif
-#ifndef MOE_DN_SKIP
-#define MOE_DN_SKIP 0
-#endif
+constexpr int kSgCk = 64;
+constexpr int kSgMinw = 4;
+constexpr bool kSgSkip = true;
+constexpr int kDnCk = 64;
+constexpr int kDnMinw = 4;
+constexpr bool kDnSkip = false;
 // Weights are read exactly once per launch.  On the tiled layout every load
 // is a whole contiguous 1 KB piece, and nontemporal loads stream those
 // faster from HBM; on row-major rows (64-byte pieces of 16 rows per load)
 // they are slower, so they are used for tiles only.
-#ifndef MOE_SG_NT
-#define MOE_SG_NT 1
-#endif
 
 template <bool TL>
 __device__ __forceinline__ u32x4 load_stream(const unsigned char* ptr) {
   const u32x4* p = reinterpret_cast<const u32x4*>(ptr);
-  if constexpr (TL && MOE_SG_NT) return __builtin_nontemporal_load(p);
+  if constexpr (TL) return __builtin_nontemporal_load(p);
   return *p;
 }
 
@@ -78,7 +59,7 @@ __global__ void __launch_bounds__(64 * WAVES, MINW) stream_gemm_kernel(GroupedPa
   constexpr int MROWS = 64;                  // rows per pass
   constexpr int A_TOTAL = MROWS * CK * 2 / 16;  // 16-byte A pieces per chunk
   constexpr int A_PIECES = (A_TOTAL + kSgThreads - 1) / kSgThreads;  // per thread
-  constexpr bool SKIP = (EPI == EPI_SWIGLU) ? MOE_SG_SKIP : MOE_DN_SKIP;
+  constexpr bool SKIP = (EPI == EPI_SWIGLU) ? kSgSkip : kDnSkip;
   static_assert(A_PIECES >= 1, "chunk too small");
   static_assert(BSRC != B_FP8 || CK <= 128, "one fp8 scale block per chunk");
   static_assert(BSRC != B_FP8 || CK >= 64, "fp8 chunks hold whole 16-byte loads per lane");
@@ -362,13 +343,9 @@ __global__ void __launch_bounds__(kThreads) splitk_reduce_kernel(GroupedParams p
 // the decode Mixtral layer (h = 14336, 8 experts): 896 workgroups of 8
 // waves are 1.75 rounds of 2 per CU, 1024 of 7 waves exactly 2; GEMM 1
 // takes 308 instead of 329 us (14-wave workgroups, 1 round: 318 us).
-#ifndef MOE_SG_WAVES_RULE
-#define MOE_SG_WAVES_RULE 1
-#endif
 int stream_waves(int out_cols, int ngroups, int ksplit) {
-  if (!MOE_SG_WAVES_RULE || out_cols % (16 * MOE_SG_WAVES_ALT) != 0) return MOE_SG_WAVES;
-  if (MOE_SG_WAVES_RULE == 2) return MOE_SG_WAVES_ALT;
-  const int64_t slots_per_cu = 4 * MOE_SG_MINW;  // resident waves per CU at the VGPR budget
+  if (out_cols % (16 * kSgWavesAlt) != 0) return kSgWaves;
+  const int64_t slots_per_cu = 4 * kSgMinw;  // resident waves per CU at the VGPR budget
   const int64_t cus = device_info().cus;
   auto frac_tail = [&](int w) {  // fraction of the last round's slots that are busy
     const int64_t per = cus * (slots_per_cu / w);
@@ -376,12 +353,12 @@ int stream_waves(int out_cols, int ngroups, int ksplit) {
     const int64_t r = wg % per;
     return r == 0 ? 1.0 : (double)r / per;
   };
-  return frac_tail(MOE_SG_WAVES_ALT) > frac_tail(MOE_SG_WAVES) ? MOE_SG_WAVES_ALT : MOE_SG_WAVES;
+  return frac_tail(kSgWavesAlt) > frac_tail(kSgWaves) ? kSgWavesAlt : kSgWaves;
 }
 
 template <int BSRC, int EPI, int CK, int WAVES>
 moe_status launch_stream_w(const GroupedParams& p, int ngroups, int out_cols, hipStream_t stream) {
-  constexpr int MW = EPI == EPI_SWIGLU ? MOE_SG_MINW : MOE_DN_MINW;
+  constexpr int MW = EPI == EPI_SWIGLU ? kSgMinw : kDnMinw;
   auto kern = p.b_tiled ? stream_gemm_kernel<BSRC, EPI, CK, MW, true, WAVES>
                         : stream_gemm_kernel<BSRC, EPI, CK, MW, false, WAVES>;
   constexpr size_t lds = 2 * 64 * (CK * 2 + 16);
@@ -398,10 +375,10 @@ moe_status launch_stream(const GroupedParams& p, hipStream_t stream) {
   const int out_cols = (EPI == EPI_SWIGLU) ? p.N / 2 : p.N;
   if (ngroups == 0) return MOE_OK;
   moe_status st;
-  if (EPI == EPI_SWIGLU && stream_waves(out_cols, ngroups, p.ksplit) == MOE_SG_WAVES_ALT)
-    st = launch_stream_w<BSRC, EPI, CK, MOE_SG_WAVES_ALT>(p, ngroups, out_cols, stream);
+  if (EPI == EPI_SWIGLU && stream_waves(out_cols, ngroups, p.ksplit) == kSgWavesAlt)
+    st = launch_stream_w<BSRC, EPI, CK, kSgWavesAlt>(p, ngroups, out_cols, stream);
   else
-    st = launch_stream_w<BSRC, EPI, CK, MOE_SG_WAVES>(p, ngroups, out_cols, stream);
+    st = launch_stream_w<BSRC, EPI, CK, kSgWaves>(p, ngroups, out_cols, stream);
   if (st != MOE_OK) return st;
   if (p.ksplit > 1) {
     const int64_t n4 = p.prow_total * (out_cols / 4);
@@ -417,22 +394,18 @@ moe_status launch_stream(const GroupedParams& p, hipStream_t stream) {
 // long K), in powers of two that divide the chunk count.
 }  // namespace
 
-#ifndef MOE_MAX_KSPLIT
-#define MOE_MAX_KSPLIT 4
-#endif
-#ifndef MOE_KSPLIT_WAVES_PER_CU
-#define MOE_KSPLIT_WAVES_PER_CU 12
-#endif
+constexpr int kMaxKsplit = 4;
+constexpr int kKsplitWavesPerCu = 12;
 int stream_ksplit(int ngroups, int out_cols, int K, int CK) {
   const int64_t waves = (int64_t)ngroups * (out_cols / 16);
-  const int64_t target = (int64_t)device_info().cus * MOE_KSPLIT_WAVES_PER_CU;
+  const int64_t target = (int64_t)device_info().cus * kKsplitWavesPerCu;
   int ks = 1;
-  while (ks < MOE_MAX_KSPLIT && waves * ks < target && (K / CK) % (2 * ks) == 0) ks *= 2;
+  while (ks < kMaxKsplit && waves * ks < target && (K / CK) % (2 * ks) == 0) ks *= 2;
   return ks;
 }
 
 int stream_ck_for(bool swiglu, int K) {
-  const int ck = swiglu ? MOE_SG_CK : MOE_DN_CK;
+  const int ck = swiglu ? kSgCk : kDnCk;
   return K % ck == 0 ? ck : 128;
 }
 
@@ -441,7 +414,7 @@ namespace {
 
 template <int BSRC, int EPI>
 moe_status launch_stream_k(const GroupedParams& p, hipStream_t s) {
-  constexpr int CK0 = EPI == EPI_SWIGLU ? MOE_SG_CK : MOE_DN_CK;
+  constexpr int CK0 = EPI == EPI_SWIGLU ? kSgCk : kDnCk;
   constexpr int CK = (BSRC == B_FP8 && CK0 < 64) ? 64 : CK0;
   if (p.K % CK == 0) return launch_stream<BSRC, EPI, CK>(p, s);
   return launch_stream<BSRC, EPI, 128>(p, s);

@@ -180,6 +180,17 @@ def make_workload(cfg: int, **over) -> Workload:
         elif off is not None and off[0] == "zipf":
             s = off[1]
             wl.b_router = np.array([(e + 1.0) ** (-s) for e in range(E)], dtype=np.float32)
+        elif off is not None and off[0] == "zipf_log":
+            # the logarithm of the Zipf weights (an alternative reading of
+            # the Switch workload's offset; far heavier skew)
+            s = off[1]
+            wl.b_router = np.array([-s * math.log(e + 1.0) for e in range(E)], dtype=np.float32)
+        elif off is not None and off[0] == "zipf_pmf":
+            # the normalised Zipf probabilities (another alternative reading;
+            # mild skew)
+            s = off[1]
+            w = np.array([(e + 1.0) ** (-s) for e in range(E)])
+            wl.b_router = (w / w.sum()).astype(np.float32)
         if c["select_bias"] is not None:
             wl.b_select = (torch.randn((E,), generator=gen) * c["select_bias"]).numpy().astype(np.float32)
         experts = [_draw_expert(gen, d, h, wl.act, c["w_std"], wl.w_dtype) for _ in range(nx)]
