@@ -34,9 +34,13 @@ def test_traffic_only_while_sources_and_layout_match(monkeypatch):
         rec = json.load(open(path))
         monkeypatch.setattr(B, "sources_sha256", lambda files, r=rec: r["source_sha256"])
         assert B.traffic_from_profiles(cfg, rec["w_layout"]) == rec["bytes_per_launch"]
-        # the counters cover at most a few percent above the algorithmic
-        # bytes: no large re-read
-        assert 0.95 <= rec["bytes_per_launch"] / rec["algorithmic_bytes_per_launch"] < 1.5
+        # the recorded bytes are the calibrated counters, and at least the
+        # bytes the kernel must move
+        cal = rec["copy_calibration"]
+        want = (rec["fetch_size_kib_per_dispatch"] * 1024 * cal["fetch_factor"] +
+                rec["write_size_kib_per_dispatch"] * 1024 * cal["write_factor"])
+        assert abs(rec["bytes_per_launch"] - want) <= 1024
+        assert rec["bytes_per_launch"] >= 0.95 * rec["algorithmic_bytes_per_launch"]
         other = "rowmajor" if rec["w_layout"] == "tiled" else "tiled"
         assert B.traffic_from_profiles(cfg, other) is None
         monkeypatch.setattr(B, "sources_sha256", lambda files: "0" * 64)
