@@ -17,13 +17,14 @@
 //    compiler does not track these waits, they are issued explicitly.
 //  * 256x256 main loop: one barrier per stage, between its two 16-k steps.
 //    The MFMAs of one step run while the fragments of the next step are
-//    read from LDS, so no MFMA waits on an LDS read issued just before it
-//    (with both waves of a SIMD waiting on their reads at once, the matrix
-//    core idled; LDS reads themselves overlap MFMAs fully when nothing waits
-//    on them).  What still costs time is the LDS-DMA writes contending with
-//    the fragment reads: measured on this chip, DMA, fragment reads and
-//    MFMAs at this kernel's ratio (4 KB DMA, 12 KB of reads and 16 MFMAs per
-//    wave) sustain ~70% of the MFMA rate, half the DMA per MFMA ~96%.
+//    read from LDS and the DMA of a later stage is issued, one read and one
+//    load instruction after each MFMA in an order fixed with sched_barrier
+//    fences.  Measured with timing-only variants: the barrier costs ~1%;
+//    the LDS-DMA costs ~17% (its writes contend with the fragment reads:
+//    the loop without global loads takes 5.35 instead of 6.4 ms on the
+//    prefill GEMM 1), and neither deeper prefetch nor one barrier per two
+//    stages helps.  4-wave 128x128 tiles (a third less LDS reading) are
+//    slower here: with one wave per SIMD its own LDS reads are not hidden.
 //  * 128x256 main loop (and the split-K router GEMM): one barrier at the
 //    top of each stage, the stage's fragments read, then its MFMAs; two
 //    workgroups per CU overlap one another's waits.
@@ -46,6 +47,8 @@
 //    the same output columns inside each wave.
 #include <math.h>
 
+#include <type_traits>
+
 #include "gemm_common.h"
 
 namespace moe {
@@ -57,6 +60,32 @@ constexpr int kMaxFp8K = 16384;  // fp8 weights: K per GEMM (the tile's scales s
 constexpr int kGM = 4;       // m-tiles per strip
 
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+// Order in which one k-step's fragments are read: by first use in the
+// i-major MFMA order (A subtile i, B subtile j), so the first MFMAs of the
+// next step wait only for the first reads; B skipped when !WITH_B.
+template <int QM, int QN, bool WITH_B>
+struct ReadOrder {
+  int n = 0;
+  int kind[QM + QN] = {};  // 0: A, 1: B
+  int idx[QM + QN] = {};
+  constexpr ReadOrder() {
+    bool sa[QM] = {}, sb[QN] = {};
+    for (int m = 0; m < QM * QN; ++m) {
+      const int i = m / QN, j = m % QN;
+      if (!sa[i]) {
+        sa[i] = true;
+        kind[n] = 0;
+        idx[n++] = i;
+      }
+      if (WITH_B && !sb[j]) {
+        sb[j] = true;
+        kind[n] = 1;
+        idx[n++] = j;
+      }
+    }
+  }
+};
 
 // Output elements are written once per launch.  The first GEMM's
 // activations (read back only by the second GEMM, after the whole first one)
@@ -144,7 +173,7 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
   // 8-wave 256x256 tiles: one barrier per stage, in the middle (see below)
   constexpr bool kMB = NW == 8 && BM == 256 && !PART;
   // stages of DMA issued before a tile's main loop
-  constexpr int kPre = kMB ? NS : NS - 1;
+  constexpr int kPre = NS - 1;
   constexpr int kThreads = 64 * NW;
   constexpr int WTM = BM / WM_, WTN = BN / WN_;  // wave tile
   constexpr int QM = WTM / 32, QN = WTN / 32;    // 32x32 subtiles per wave
@@ -167,7 +196,7 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
-  const int wave = tid / 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // uniform: LDS addresses in SGPRs
   const int wm = wave / WN_, wn = wave % WN_;
   const int ngroups = p.n_routed + (p.t_dense > 0 ? 1 : 0);
   const int nt = p.N / BN;
@@ -381,41 +410,48 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
       // stage placed between the stage's two 16-k steps.  The MFMAs of one
       // step run while the fragments of the next step are read from LDS, so
       // no MFMA waits for an LDS read issued just before it:
-      //   step 0 of stage kt: MFMAs on X (step 0 of kt) | read Y = step 1 of kt
+      //   step 0 of stage kt: MFMAs on X (step 0 of kt) | read Y = step 1 of
+      //            kt | DMA of stage kt + NS - 1 into the slot of stage kt - 1
       //   barrier: every wave's DMA of stage kt + 1 has landed and its reads
       //            of stage kt have returned, so stage kt + 1 is visible and
       //            the slot of stage kt is free
-      //   DMA of stage kt + NS into the slot of stage kt
       //   step 1 of stage kt: MFMAs on Y | read X = step 0 of kt + 1
+      // Inside a step, MFMA q is followed by the q-th fragment read and the
+      // q-th DMA instruction, each group fenced with sched_barrier: left to
+      // itself the compiler bunches the reads and loads behind one MFMA and
+      // the matrix core idles while they issue (measured: prefill GEMM 1
+      // 7.2 -> 6.4 ms).
       // fp8 weights: a lane's 16 B fragment bytes hold both steps of a stage,
       // read with step 0 and converted to bf16 after the step-1 MFMAs.
       u32x4 aX[QM], aY[QM], bX[QN], bY[QN];
       uint32_t raw[QN][4];
-      auto rd_a = [&](int kt, int step, u32x4 (&aq)[QM]) {
+      // A fragment of subtile i, k-step `step`, stage kt
+      auto rd_a1 = [&](int kt, int step, int i) {
         const unsigned char* st = ring + (kt % NS) * STAGE_BYTES;
         const int c = 2 * h + step;  // A chunk: k [16h + 8 step, +8)
+        const int R = wm * WTM + i * 32 + (lane & 31), r = R & 15;
+        return *reinterpret_cast<const u32x4*>(st + (R >> 4) * 1024 + (r * 4 + (c ^ swz(r))) * 16);
+      };
+      // B fragment of subtile j; fp8: the raw bytes of both steps into raw[j]
+      auto rd_b1 = [&](int kt, int step, int j, u32x4& bq) {
+        const unsigned char* st = ring + (kt % NS) * STAGE_BYTES;
+        const int R = wn * WTN + j * 32 + (lane & 31), r = R & 15;
+        if constexpr (F8) {
+          const int boff = TL ? ((R >> 4) & 1) * 512 + (16 * h + r) * 16 : (R & 31) * 32 + h * 16;
+          const u32x4 w8 = *reinterpret_cast<const u32x4*>(st + A_BYTES + (R >> 5) * 1024 + boff);
 #pragma unroll
-        for (int i = 0; i < QM; ++i) {
-          const int R = wm * WTM + i * 32 + (lane & 31), r = R & 15;
-          aq[i] = *reinterpret_cast<const u32x4*>(st + (R >> 4) * 1024 + (r * 4 + (c ^ swz(r))) * 16);
+          for (int q = 0; q < 4; ++q) raw[j][q] = w8[q];
+        } else {
+          const int c = 2 * h + step;
+          const int boff = TL ? (16 * c + r) * 16 : (r * 4 + (c ^ swz(r))) * 16;
+          bq = *reinterpret_cast<const u32x4*>(st + A_BYTES + (R >> 4) * 1024 + boff);
         }
       };
-      auto rd_b = [&](int kt, int step, u32x4 (&bq)[QN]) {
-        const unsigned char* st = ring + (kt % NS) * STAGE_BYTES;
-#pragma unroll
-        for (int j = 0; j < QN; ++j) {
-          const int R = wn * WTN + j * 32 + (lane & 31), r = R & 15;
-          if constexpr (F8) {
-            const int boff = TL ? ((R >> 4) & 1) * 512 + (16 * h + r) * 16 : (R & 31) * 32 + h * 16;
-            const u32x4 w8 = *reinterpret_cast<const u32x4*>(st + A_BYTES + (R >> 5) * 1024 + boff);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) raw[j][q] = w8[q];
-          } else {
-            const int c = 2 * h + step;
-            const int boff = TL ? (16 * c + r) * 16 : (r * 4 + (c ^ swz(r))) * 16;
-            bq[j] = *reinterpret_cast<const u32x4*>(st + A_BYTES + (R >> 4) * 1024 + boff);
-          }
-        }
+      // DMA instruction i of stage kt (as in issue())
+      auto dma1 = [&](int kt, int i) {
+        unsigned char* st = ring + (kt % NS) * STAGE_BYTES;
+        __builtin_amdgcn_global_load_lds(MOE_GPTR(cur.src[i] + (int64_t)kt * cur.kstep[i]),
+                                         MOE_LPTR(st + (wave + NW * i) * 1024), 16, 0, 0);
       };
       // fp8: raw bytes of stage kt -> bf16 B fragments of both steps
       auto cvt_b = [&](int kt) {
@@ -447,48 +483,60 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
           }
         }
       };
-      auto mma = [&](const u32x4 (&aq)[QM], const u32x4 (&bq)[QN]) {
+      // One 16-k step: the QM x QN MFMAs on (aq, bq); after MFMA q the q-th
+      // read of the fragments (an, bn) of k-step step_rd of stage kt_rd and,
+      // with DMA, the q-th load instruction of stage kt_dma.
+      auto step = [&](const u32x4 (&aq)[QM], const u32x4 (&bq)[QN], u32x4 (&an)[QM],
+                      u32x4 (&bn)[QN], int kt_rd, int step_rd, auto with_b, int kt_dma,
+                      auto dma) {
+        constexpr ReadOrder<QM, QN, decltype(with_b)::value> ord{};
+        static_assert(ord.n <= QM * QN && LPW <= QM * QN, "one read and one load per MFMA");
 #pragma unroll
-        for (int i = 0; i < QM; ++i)
-#pragma unroll
-          for (int j = 0; j < QN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8_t, aq[i]), __builtin_bit_cast(bf16x8_t, bq[j]), acc[i][j],
-                0, 0, 0);
+        for (int q = 0; q < QM * QN; ++q) {
+          const int i = q / QN, j = q % QN;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, aq[i]), __builtin_bit_cast(bf16x8_t, bq[j]), acc[i][j], 0,
+              0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          if (q < ord.n) {
+            if (ord.kind[q] == 0) an[ord.idx[q]] = rd_a1(kt_rd, step_rd, ord.idx[q]);
+            else rd_b1(kt_rd, step_rd, ord.idx[q], bn[ord.idx[q]]);
+          }
+          if constexpr (decltype(dma)::value)
+            if (q < LPW) dma1(kt_dma, q);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       };
-      wait_dma_and_barrier<LPW>(min(NS - 1, KT - 1));  // stage 0 visible
-      rd_a(0, 0, aX);
-      rd_b(0, 0, bX);
-      if constexpr (F8) cvt_b(0);
-      for (int kt = 0; kt < KT; ++kt) {
-        // step 0 of stage kt; read step 1
-        rd_a(kt, 1, aY);
-        if constexpr (!F8) rd_b(kt, 1, bY);
-        mma(aX, bX);
-        constexpr int kR1 = F8 ? QM : QM + QN;
-#pragma unroll
-        for (int r = 0; r < kR1; ++r) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, QM * QN - kR1, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        wait_dma_and_barrier<LPW>(min(NS - 2, KT - 2 - kt));
-        if (kt + NS < KT) issue(cur, kt + NS);
-        // step 1 of stage kt; read step 0 of stage kt + 1 (at the last stage
-        // a slot whose contents are not used)
-        rd_a(kt + 1, 0, aX);
-        rd_b(kt + 1, 0, bX);
-        mma(aY, bY);
-        constexpr int kR2 = QM + QN;
-#pragma unroll
-        for (int r = 0; r < kR2; ++r) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, QM * QN - kR2, 0);
-        __builtin_amdgcn_sched_barrier(0);
+      // step 0 of stage kt (fp8: the B bytes of both steps came with step 0)
+      auto step0 = [&](int kt, auto dma) {
+        step(aX, bX, aY, bY, kt, 1, std::integral_constant<bool, !F8>{}, kt + NS - 1, dma);
+      };
+      // step 1 of stage kt; at the last stage it reads a slot whose contents
+      // are not used
+      auto step1 = [&](int kt) {
+        step(aY, bY, aX, bX, kt + 1, 0, std::true_type{}, 0, std::false_type{});
         if constexpr (F8) cvt_b(kt + 1);
+      };
+      wait_dma_and_barrier<LPW>(min(NS - 2, KT - 1));  // stage 0 visible
+#pragma unroll
+      for (int i = 0; i < QM; ++i) aX[i] = rd_a1(0, 0, i);
+#pragma unroll
+      for (int j = 0; j < QN; ++j) rd_b1(0, 0, j, bX[j]);
+      if constexpr (F8) cvt_b(0);
+      // every stage but the last NS - 1 loads stage kt + NS - 1, so NS - 2
+      // later stages are in flight at each of these barriers
+      int kt = 0;
+      for (; kt < KT - NS + 1; ++kt) {
+        step0(kt, std::true_type{});
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((NS - 2) * LPW) : "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        step1(kt);
+      }
+      for (; kt < KT; ++kt) {
+        step0(kt, std::false_type{});
+        wait_dma_and_barrier<LPW>(min(NS - 2, KT - 2 - kt));
+        __builtin_amdgcn_sched_barrier(0);
+        step1(kt);
       }
     } else
     for (int kt = 0; kt < KT; ++kt) {
