@@ -25,9 +25,12 @@
 //    prefill GEMM 1), and neither deeper prefetch nor one barrier per two
 //    stages helps.  4-wave 128x128 tiles (a third less LDS reading) are
 //    slower here: with one wave per SIMD its own LDS reads are not hidden.
-//  * 128x256 main loop (and the split-K router GEMM): one barrier at the
-//    top of each stage, the stage's fragments read, then its MFMAs; two
-//    workgroups per CU overlap one another's waits.
+//  * 128x256 tiles (two workgroups per CU) run the same loop (Switch
+//    workload GEMM 1 351 -> 336 us); there the short K (1024) leaves the
+//    per-tile work (GELU epilogue, stores, pipeline refill) at ~45% of the
+//    time: without any loads in the loop GEMM 1 still takes 250 us.  The
+//    split-K router GEMM keeps one barrier at the top of each stage, the
+//    stage's fragments read, then its MFMAs.
 //  * Every wave instruction fills 1 KB of LDS.  Row-major 16-bit operands:
 //    16 tile rows x 64 bytes, four consecutive lanes per row (full 64-byte
 //    global segments); inside the block the 16-byte chunks of row r are
@@ -170,8 +173,10 @@ template <int BSRC, bool TL, int EPI, int BM, int BN, int WM_, int WN_, int NS, 
 __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedParams p) {
   constexpr bool F8 = BSRC == B_FP8;
   constexpr int NW = WM_ * WN_;                  // waves
-  // 8-wave 256x256 tiles: one barrier per stage, in the middle (see below)
-  constexpr bool kMB = NW == 8 && BM == 256 && !PART;
+  // 256x256 tiles of 8 waves and 128x256 tiles of 4 waves (two workgroups
+  // per CU), both 128x64 per wave: one barrier per stage, in the middle
+  // (see below)
+  constexpr bool kMB = ((NW == 8 && BM == 256) || (NW == 4 && BM == 128)) && BN == 256 && !PART;
   // stages of DMA issued before a tile's main loop
   constexpr int kPre = NS - 1;
   constexpr int kThreads = 64 * NW;
@@ -406,10 +411,11 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
         for (int r = 0; r < kScRegs; ++r) asm volatile("" ::"v"(cur.sr[j][r]));
     }
     if constexpr (kMB) {
-      // Two waves per SIMD, 128x64 per wave, one workgroup barrier per
-      // stage placed between the stage's two 16-k steps.  The MFMAs of one
-      // step run while the fragments of the next step are read from LDS, so
-      // no MFMA waits for an LDS read issued just before it:
+      // Two waves per SIMD (one workgroup of 8, or two of 4), 128x64 per
+      // wave, one workgroup barrier per stage placed between the stage's two
+      // 16-k steps.  The MFMAs of one step run while the fragments of the
+      // next step are read from LDS, so no MFMA waits for an LDS read issued
+      // just before it:
       //   step 0 of stage kt: MFMAs on X (step 0 of kt) | read Y = step 1 of
       //            kt | DMA of stage kt + NS - 1 into the slot of stage kt - 1
       //   barrier: every wave's DMA of stage kt + 1 has landed and its reads
