@@ -335,15 +335,18 @@ def main():
     value = wl.T * K / wall
 
     # Stage breakdown, after the timed region: an event at every stage
-    # boundary, and before each such step a 512 MiB write that evicts the
+    # boundary, and before each such step a 512 MiB read that evicts the
     # layer's buffers from the 256 MB Infinity Cache (outside the events), so
     # every stage starts cache-cold as in a model where other layers run in
-    # between.
+    # between.  The eviction reads (a sum) rather than writes: a write would
+    # leave the caches full of dirty lines whose write-back the first stage
+    # would pay for.
     KB = min(K, 20)
-    flush = torch.empty((MALL_FLUSH_MIB << 20,), dtype=torch.uint8, device="cuda:0")
+    flush = torch.ones((MALL_FLUSH_MIB << 18,), dtype=torch.int32, device="cuda:0")
+    flush.sum()
     ev = Events(hip, n * KB)
     for s in range(KB):
-        flush.fill_(s & 0xFF)
+        flush.sum()
         layer.forward(events=ev.ev[s * n:(s + 1) * n])
     torch.cuda.synchronize()
     del flush
@@ -414,7 +417,7 @@ def main():
         "gemm1_ms_timed": gemm1_ms,
         "stages_ms": stage_ms,
         "stages_note": (f"stage times from {KB} further steps with an event at every stage "
-                        f"boundary, each after a {MALL_FLUSH_MIB} MiB write that flushes the "
+                        f"boundary, each after a {MALL_FLUSH_MIB} MiB read that flushes the "
                         f"Infinity Cache ({step_cold_ms:.4f} ms per such step)"),
         "ms_per_step_cache_cold": step_cold_ms,
         "stages_hbm_frac": stage_frac,

@@ -9,10 +9,16 @@
 // balancing bullet): it enters the selection key and nothing else.
 //
 // Kernels
-//   route_small_kernel : E <= 8 and W_r fits in LDS.  One pass over x with
-//                        W_r staged in LDS, fp32 VALU dot products, wave
-//                        butterfly reduction, top-k and weights fused.  The
-//                        op is HBM-bound (2E/s_a <= 8 flop per byte of x).
+//   route_mfma_kernel  : bf16, E <= 32, many tokens.  Logits on the matrix
+//                        cores (x by DMA through per-wave LDS rings), top-k
+//                        and weights fused.  Measured on the prefill workload
+//                        (E = 8, d = 4096): 37 us, against 70 us for the
+//                        VALU kernel below, whose FMAs and bf16 widening
+//                        limited it well below the HBM rate.
+//   route_small_kernel : E <= 8 and W_r fits in LDS (fp32, or few tokens).
+//                        One pass over x with W_r staged in LDS, fp32 VALU
+//                        dot products, wave butterfly reduction, top-k and
+//                        weights fused.
 //   logits_valu_kernel : any E, W_r read through L2; writes fp32 logits.
 //   topk_kernel        : one wave per token over fp32 logits in memory,
 //                        E <= 256; wavefront-shuffle arg-max k times.
@@ -23,6 +29,7 @@
 
 #include "common.h"
 #include "gemm.h"
+#include "gemm_common.h"
 
 namespace moe {
 namespace {
@@ -602,6 +609,76 @@ __device__ __forceinline__ float row_sum_f32(float v) {
 // a round stays inside the row (DPP row moves, no cross-row step), and the
 // chosen expert's value comes from its lane with one bpermute.  Same
 // selection order, keys and weights as topk_kernel.
+// Selection and weights of the token of one 16-lane row (topk_rows_kernel,
+// route_mfma_kernel): lane `sub` holds the final logits L[i] of experts
+// sub + 16 i (i < 4; entries past E are ignored).
+__device__ __forceinline__ void rows_select(const float (&L)[4], int sub, int row0, int64_t t,
+                                            int E, int k, int score, int renorm,
+                                            const float* __restrict__ b_select,
+                                            int32_t* __restrict__ ids,
+                                            float* __restrict__ weights) {
+  constexpr int PER = 4, RL = 16;
+  float sc[PER];
+  uint64_t pk[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = sub + i * RL;
+    float key;
+    if (score == MOE_SIGMOID) {
+      sc[i] = sigmoid_f32_via_f64(L[i]);
+      key = (b_select && e < E) ? sc[i] + b_select[e] : sc[i];
+    } else {
+      sc[i] = 0.f;
+      key = L[i];
+    }
+    pk[i] = e < E ? ((uint64_t)key_image(key) << 32) | (uint32_t)(0xffffffffu - (uint32_t)e) : 0ull;
+  }
+  int sel_e = -1;
+  float sel_v = 0.f, first_logit = 0.f;
+  for (int j = 0; j < k; ++j) {
+    uint64_t mine = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) mine = pk[i] > mine ? pk[i] : mine;
+    const uint64_t win = row_max_u64(mine);
+    const int bi = (int)(0xffffffffu - (uint32_t)win);  // uniform within the row
+    const int owner = bi & (RL - 1), slot = bi / RL;
+    float v = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (i == slot) {
+        v = (score == MOE_SIGMOID) ? sc[i] : L[i];
+        if (sub == owner) pk[i] = 0;
+      }
+    const float bv = __shfl(v, row0 + owner, kWave);
+    if (sub == j) {
+      sel_e = bi;
+      sel_v = bv;
+    }
+    if (j == 0) first_logit = bv;
+  }
+  float num, denom;
+  if (score == MOE_SOFTMAX) {
+    num = (sub < k) ? __expf(sel_v - first_logit) : 0.f;
+    if (renorm) {
+      denom = num;
+    } else {
+      denom = 0.f;
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (sub + i * RL < E) denom += __expf(L[i] - first_logit);
+    }
+  } else {
+    num = (sub < k) ? sel_v : 0.f;
+    denom = num;
+  }
+  denom = row_sum_f32(denom);
+  if (score == MOE_SIGMOID && !renorm) denom = 1.f;
+  if (sub < k) {
+    ids[t * k + sub] = sel_e;
+    weights[t * k + sub] = num / denom;
+  }
+}
+
 template <int KS>
 __global__ void __launch_bounds__(256) topk_rows_kernel(
     const float* __restrict__ logits_in, const float* __restrict__ b_router,
@@ -622,8 +699,7 @@ __global__ void __launch_bounds__(256) topk_rows_kernel(
 #pragma unroll
       for (int z = 0; z < KS; ++z) part[i][z] = logits_in[(int64_t)z * T_tok * E + t * E + ec];
     }
-    float L[PER], sc[PER];
-    uint64_t pk[PER];
+    float L[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int e = sub + i * RL;
@@ -632,61 +708,168 @@ __global__ void __launch_bounds__(256) topk_rows_kernel(
       for (int z = 1; z < KS; ++z) l += part[i][z];
       L[i] = l + ((b_router && e < E) ? b_router[e] : 0.f);
       if (logits_out && e < E) logits_out[t * E + e] = L[i];
-      float key;
-      if (score == MOE_SIGMOID) {
-        sc[i] = sigmoid_f32_via_f64(L[i]);
-        key = (b_select && e < E) ? sc[i] + b_select[e] : sc[i];
-      } else {
-        sc[i] = 0.f;
-        key = L[i];
-      }
-      pk[i] = e < E ? ((uint64_t)key_image(key) << 32) | (uint32_t)(0xffffffffu - (uint32_t)e) : 0ull;
     }
-    int sel_e = -1;
-    float sel_v = 0.f, first_logit = 0.f;
-    for (int j = 0; j < k; ++j) {
-      uint64_t mine = 0;
+    rows_select(L, sub, row0, t, E, k, score, renorm, b_select, ids, weights);
+  }
+}
+
+// ---------------------------------------------------------------- E <= 64, bf16, many tokens
+// Logits on the matrix cores, top-k fused.  A workgroup of four waves takes
+// 32 tokens at a time; each wave runs v_mfma_f32_32x32x16_bf16 over a
+// quarter of d, with the tokens as M and up to 64 experts as N (one or two
+// 32-wide tiles; rows past E are zero).  x reaches the wave through its own
+// LDS ring by DMA (buffer_load ... lds, 16 token rows x 64 bytes per
+// instruction, the 16-byte chunks of row r placed at chunk c ^ h(r) so the
+// fragment reads are conflict-free); only the wave itself reads its ring,
+// so an s_waitcnt suffices, no barrier.  W_r (a few hundred KB at most,
+// L2-resident) is read straight into B fragments.  x blocks of 32 k and
+// their W_r fragments are loaded seven blocks ahead; the next tile's first
+// blocks are in flight while the current tile's partial logits are summed
+// through LDS (16 tokens at a time) and each token is selected by one
+// 16-lane row as in topk_rows_kernel.
+constexpr int kRmWaves = 4;
+constexpr int kRmRing = 8;          // x blocks per wave ring (seven ahead)
+constexpr int kRmBlock = 32 * 64;   // bytes of one block: 32 rows x 32 k
+
+__host__ __device__ constexpr size_t rm_lds_bytes(int E) {
+  return (size_t)kRmWaves * kRmRing * kRmBlock + (size_t)(kRmWaves * 16 + 2) * E * sizeof(float);
+}
+
+__device__ __forceinline__ int rm_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+template <int NT>
+__global__ void __launch_bounds__(64 * kRmWaves, 2) route_mfma_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ wr, const float* __restrict__ b_router,
+    const float* __restrict__ b_select, float* __restrict__ logits_out, int32_t* __restrict__ ids,
+    float* __restrict__ weights, int64_t T_tok, int d, int E, int k, int score, int renorm) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  unsigned char* ring = smem_raw + wave * kRmRing * kRmBlock;
+  float* part = reinterpret_cast<float*>(smem_raw + kRmWaves * kRmRing * kRmBlock);  // [w][16][E]
+  float* s_brouter = part + kRmWaves * 16 * E;
+  float* s_bselect = s_brouter + E;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    s_brouter[e] = b_router ? b_router[e] : 0.f;
+    s_bselect[e] = b_select ? b_select[e] : 0.f;
+  }
+  const int h = lane >> 5;
+  const int sub = lane & 15, row0 = lane & ~15;
+  const int nbw = d / 32 / kRmWaves;  // 32-k blocks of this wave's quarter of d
+  const int kb0 = wave * nbw;
+  const int64_t tiles = (T_tok + 31) / 32;
+  // DMA lane role: row dr of the 16 of an instruction, logical chunk dc
+  const int dr = lane >> 2, dc = (lane & 3) ^ rm_swz(lane >> 2);
+  // B fragment rows: expert nt * 32 + (lane & 31), clamped (zeroed past E)
+  const bf16_t* wrow[NT];
+  bool bval[NT];
 #pragma unroll
-      for (int i = 0; i < PER; ++i) mine = pk[i] > mine ? pk[i] : mine;
-      const uint64_t win = row_max_u64(mine);
-      const int bi = (int)(0xffffffffu - (uint32_t)win);  // uniform within the row
-      const int owner = bi & (RL - 1), slot = bi / RL;
-      float v = 0.f;
+  for (int nt = 0; nt < NT; ++nt) {
+    const int e = nt * 32 + (lane & 31);
+    bval[nt] = e < E;
+    wrow[nt] = wr + (int64_t)min(e, E - 1) * d;
+  }
+  u32x4 wb[kRmRing][NT][2];  // W_r fragments of the ring's blocks, both k-steps
+  // block blk (< nbw) of tile tl into ring slot `slot`: two DMA instructions
+  // (rows 0-15, 16-31; tokens past T re-read the last row) and the W_r
+  // fragments.  Exactly 2 + 2 NT vector-memory instructions.
+  auto fetch = [&](int slot, int64_t tl, int blk) {
+    const int kk = (kb0 + blk) * 32;  // first k of the block
+    // the tile's 32 rows as a raw buffer (a buffer_load ... lds, unlike
+    // global_load_lds, leaves the compiler's waits for the W_r registers
+    // exact instead of waiting for every DMA in flight)
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(x + tl * 32 * d), 0, 32 * 2 * d, 0x00020000);
 #pragma unroll
-      for (int i = 0; i < PER; ++i)
-        if (i == slot) {
-          v = (score == MOE_SIGMOID) ? sc[i] : L[i];
-          if (sub == owner) pk[i] = 0;
+    for (int i = 0; i < 2; ++i) {
+      const int64_t t = min(tl * 32 + 16 * i + dr, T_tok - 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (void __attribute__((address_space(3)))*)(ring + slot * kRmBlock + i * 1024), 16,
+          (int)((t - tl * 32) * 2 * d + (kk + dc * 8) * 2), 0, 0, 0);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        wb[slot][nt][s] = *reinterpret_cast<const u32x4*>(wrow[nt] + kk + 8 * (2 * h + s));
+  };
+  __syncthreads();  // biases staged
+  int64_t tile = blockIdx.x;
+#pragma unroll
+  for (int u = 0; u < kRmRing - 1; ++u) fetch(u, min(tile, tiles - 1), u);
+  for (; tile < tiles; tile += gridDim.x) {
+    const int64_t next = min(tile + (int64_t)gridDim.x, tiles - 1);
+    f32x16 acc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x16{};
+    // block kb + u sits in slot u (nbw is a multiple of kRmRing); with it in
+    // use, slot (u - 1) mod kRmRing is refilled with block kb + u + kRmRing - 1
+    // or, past the quarter, with the next tile's block of that index - nbw
+    for (int kb = 0; kb < nbw; kb += kRmRing) {
+#pragma unroll
+      for (int u = 0; u < kRmRing; ++u) {
+        const int nb_ = kb + u + kRmRing - 1;
+        const bool here = nb_ < nbw;
+        fetch((u + kRmRing - 1) % kRmRing, here ? tile : next, here ? nb_ : nb_ - nbw);
+        // slot u's DMA and fragments have landed: only the kRmRing - 1 later
+        // fetches may be outstanding
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kRmRing - 1) * (2 + 2 * NT)) : "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        const unsigned char* st = ring + u * kRmBlock;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int r = lane & 31, c = 2 * h + s;  // A chunk: k [16h + 8s ... of the block order
+          const u32x4 af = *reinterpret_cast<const u32x4*>(st + r * 64 + ((c ^ rm_swz(r)) * 16));
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            u32x4 bq = wb[u][nt][s];
+            if (!bval[nt]) bq = u32x4{0, 0, 0, 0};
+            acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8_t, af), __builtin_bit_cast(bf16x8_t, bq), acc[nt], 0, 0,
+                0);
+          }
         }
-      const float bv = __shfl(v, row0 + owner, kWave);
-      if (sub == j) {
-        sel_e = bi;
-        sel_v = bv;
+        // the next refill overwrites the slot read here: keep it behind
+        // these MFMAs, which waited for the reads
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (j == 0) first_logit = bv;
     }
-    float num, denom;
-    if (score == MOE_SOFTMAX) {
-      num = (sub < k) ? __expf(sel_v - first_logit) : 0.f;
-      if (renorm) {
-        denom = num;
-      } else {
-        denom = 0.f;
+    // value v of a lane: token 8 (v / 4) + 4 h + v % 4, expert nt * 32 + lane % 32
 #pragma unroll
-        for (int i = 0; i < PER; ++i)
-          if (sub + i * RL < E) denom += __expf(L[i] - first_logit);
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int e = nt * 32 + (lane & 31);
+#pragma unroll
+        for (int v = 8 * half; v < 8 * half + 8; ++v) {
+          const int r = 8 * (v / 4) + 4 * h + (v % 4) - 16 * half;
+          if (e < E) part[(wave * 16 + r) * E + e] = acc[nt][v];
+        }
       }
-    } else {
-      num = (sub < k) ? sel_v : 0.f;
-      denom = num;
-    }
-    denom = row_sum_f32(denom);
-    if (score == MOE_SIGMOID && !renorm) denom = 1.f;
-    if (sub < k) {
-      ids[t * k + sub] = sel_e;
-      weights[t * k + sub] = num / denom;
+      // LDS-only barriers here: __syncthreads would also wait for the next
+      // tile's loads in flight
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      // wave w selects tokens 4w .. 4w + 3 of the 16, one per 16-lane row
+      const int r = 4 * wave + (lane >> 4);
+      const int64_t t = tile * 32 + 16 * half + r;
+      if (t < T_tok) {
+        float L[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = min(sub + 16 * i, E - 1);
+          float l = 0.f;
+#pragma unroll
+          for (int w = 0; w < kRmWaves; ++w) l += part[(w * 16 + r) * E + e];
+          L[i] = l + s_brouter[e];
+          if (logits_out && sub + 16 * i < E) logits_out[t * E + e] = L[i];
+        }
+        rows_select(L, sub, row0, t, E, k, score, renorm, b_select ? s_bselect : nullptr, ids,
+                    weights);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the ring's last refills
 }
 
 int grid_for(int64_t units, int per_block);
@@ -759,8 +942,19 @@ bool small_route_fits(const moe_route_args* a) {
 }
 
 
+// bf16, E <= 64 without group limits, many tokens: route_mfma_kernel
+bool mfma_rows_route(const moe_route_args* a) {
+  // each wave's quarter of d is a whole number of ring rounds of 32-k blocks.
+  // E <= 32 only: at E = 64 the B fragments, two 32-row gathers from W_r per
+  // k-step, cost more than the logits GEMM + topk_rows_kernel path (Switch
+  // workload: 43 against 41 us)
+  return a->act_dtype == MOE_BF16 && a->E <= 32 && !grouped(a) &&
+         a->d % (32 * kRmWaves * kRmRing) == 0 && a->T > 1024;
+}
+
 bool mfma_route(const moe_route_args* a) {
-  return a->act_dtype == MOE_BF16 && a->E % 64 == 0 && a->d % 128 == 0 && !small_route_fits(a);
+  return a->act_dtype == MOE_BF16 && a->E % 64 == 0 && a->d % 128 == 0 && !small_route_fits(a) &&
+         !mfma_rows_route(a);
 }
 
 }  // namespace
@@ -774,7 +968,7 @@ static int route_ksplit(const moe_route_args* a) {
 }
 
 extern "C" size_t moe_route_workspace_bytes(const moe_route_args* a) {
-  if (!a || a->x == nullptr || small_route_fits(a)) return 0;
+  if (!a || a->x == nullptr || small_route_fits(a) || mfma_rows_route(a)) return 0;
   return align_up((size_t)route_ksplit(a) * a->T * a->E * sizeof(float), 256);
 }
 
@@ -819,6 +1013,18 @@ extern "C" moe_status moe_route(const moe_route_args* a, void* ws, size_t ws_byt
   const int vn = a->act_dtype == MOE_F32 ? 4 : 8;
   MOE_CHECK_ARG(a->d % vn == 0, "d must be a multiple of 16 bytes");
   MOE_CHECK_ARG(aligned16(a->x) && aligned16(a->w_router), "x/w_router not 16-byte aligned");
+  if (mfma_rows_route(a)) {
+    if (check_only()) return MOE_OK;
+    const size_t lds = rm_lds_bytes(a->E);
+    const int per_cu = 2 * lds <= 160 * 1024 ? 2 : 1;
+    const int grid = (int)std::min<int64_t>((a->T + 31) / 32, (int64_t)device_info().cus * per_cu);
+    MOE_CHECK_HIP(set_dynamic_lds((const void*)route_mfma_kernel<1>, (int)lds));
+    route_mfma_kernel<1><<<grid, 64 * kRmWaves, lds, stream>>>(
+        (const bf16_t*)a->x, (const bf16_t*)a->w_router, a->b_router, a->b_select, a->logits,
+        a->ids, a->weights, a->T, a->d, a->E, a->k, a->score, a->renorm);
+    MOE_CHECK_LAUNCH();
+    return MOE_OK;
+  }
   if (small_route_fits(a)) {
     if (check_only()) return MOE_OK;
     // Many tokens: stage W_r in LDS once per workgroup and loop over tokens.
