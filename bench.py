@@ -35,8 +35,11 @@ FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA
 # rocprofv3 FETCH_SIZE/WRITE_SIZE records of each workload's first expert
 # GEMM (per launch, calibrated against a plain copy); each is reported only
 # while the sources it lists hash to its recorded value
-TRAFFIC_RECORDS = {1: "profiles/gemm1_decode_traffic.json",
-                   2: "profiles/gemm1_prefill_traffic.json"}
+TRAFFIC_RECORDS = {0: "profiles/gemm1_snippet_traffic.json",
+                   1: "profiles/gemm1_decode_traffic.json",
+                   2: "profiles/gemm1_prefill_traffic.json",
+                   3: "profiles/gemm1_switch_traffic.json",
+                   4: "profiles/gemm1_deepseek_traffic.json"}
 MALL_FLUSH_MIB = 512           # > 2x the 256 MB Infinity Cache
 STAGES = ["route", "dispatch", "gemm1", "gemm2", "combine"]
 

@@ -45,7 +45,7 @@ def test_traffic_only_while_sources_and_layout_match(monkeypatch):
         assert B.traffic_from_profiles(cfg, other) is None
         monkeypatch.setattr(B, "sources_sha256", lambda files: "0" * 64)
         assert B.traffic_from_profiles(cfg, rec["w_layout"]) is None
-    assert B.traffic_from_profiles(0, "rowmajor") is None  # no record
+    assert B.traffic_from_profiles(99, "tiled") is None  # no record
 
 
 def test_cpu_sample_keeps_weights_and_cuts_tokens():
