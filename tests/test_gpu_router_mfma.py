@@ -22,6 +22,9 @@ CASES = [
     (2, dict(T=2085, d=1024, h=256, E=32, k=8, R=8, renorm=False)),     # E=32, no renorm
     (4, dict(T=2085, d=1024, h=256, E=32, k=8, R=8)),                   # sigmoid + bias
     (4, dict(T=3001, d=1024, h=256, E=16, k=4, R=8, renorm=False)),     # sigmoid, raw scores
+    (2, dict(T=1057, d=1024, h=256, E=3, k=2, R=1)),                    # odd E, T just past 1024
+    (4, dict(T=1100, d=1024, h=256, E=5, k=3, R=1)),                    # odd E, sigmoid + bias
+    (2, dict(T=1025, d=1024, h=256, E=1, k=1, R=1)),                    # one expert, one token past a tile
 ]
 
 
