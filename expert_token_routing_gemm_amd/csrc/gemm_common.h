@@ -69,7 +69,13 @@ __device__ __forceinline__ inline float act_gelu(float v) {
   const float q = p * __expf(-z * z);
   return 0.5f * v * (v < 0.f ? q : 2.f - q);
 }
-__device__ __forceinline__ float act_silu(float v) { return v / (1.f + __expf(-v)); }
+// SiLU with the hardware reciprocal (about 1 ulp) instead of an IEEE
+// division, which took ~10 instructions per value in the SwiGLU epilogue
+// (with the hardware bf16 rounding of the stores: prefill expert GEMM 1
+// 6.24 -> 6.15 ms).
+__device__ __forceinline__ float act_silu(float v) {
+  return v * __builtin_amdgcn_rcpf(1.f + __expf(-v));
+}
 
 template <typename CT>
 __device__ __forceinline__ void store_out(CT* p, float v);
