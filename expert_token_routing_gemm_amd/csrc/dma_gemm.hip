@@ -7,9 +7,11 @@
 // Design (MI355X-specific):
 //  * 256x256 output tile per workgroup of 8 waves (2 per SIMD); each wave
 //    owns 128x64 as 4x2 v_mfma_f32_32x32x16_bf16 subtiles (the full-rate bf16
-//    MFMA on gfx950; 128 fp32 accumulators per lane).  Groups averaging a few
-//    hundred rows (with no shared expert) use 128x256 tiles of 4 waves, two
-//    workgroups per CU.
+//    MFMA on gfx950; 128 fp32 accumulators per lane).  bf16 GEMMs without an
+//    activation use 4 waves of 128x128 (256 accumulators per lane in
+//    AccVGPRs, one wave per SIMD), each stage's DMA split over its two
+//    k-steps.  Groups averaging a few hundred rows (with no shared expert)
+//    use 128x256 tiles of 4 waves, two workgroups per CU.
 //  * Global -> LDS with global_load_lds_dwordx4 (no register staging) into
 //    a ring of 32-k stages: 4 stages of 32 KB (24 KB with fp8 weights) for
 //    256x256 tiles, 3 for 128x256.  Each wave waits for its own loads of a
@@ -65,6 +67,14 @@ constexpr int kGM = 4;       // m-tiles per strip
 constexpr int kCB = 32;      // n-tiles per column block
 
 __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+// DMA instructions a k-step issues: none (ON false), all of the stage's, or,
+// with the stage split over its two steps, the first or second half (HALF).
+template <bool ON, bool HALF>
+struct DmaTag {
+  static constexpr bool value = ON;
+  static constexpr bool half = HALF;
+};
 
 // Order in which one k-step's fragments are read: by first use in the
 // i-major MFMA order (A subtile i, B subtile j), so the first MFMAs of the
@@ -178,9 +188,14 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
   constexpr bool F8 = BSRC == B_FP8;
   constexpr int NW = WM_ * WN_;                  // waves
   // 256x256 tiles of 8 waves and 128x256 tiles of 4 waves (two workgroups
-  // per CU), both 128x64 per wave: one barrier per stage, in the middle
-  // (see below)
-  constexpr bool kMB = ((NW == 8 && BM == 256) || (NW == 4 && BM == 128)) && BN == 256 && !PART;
+  // per CU), both 128x64 per wave, and 256x256 tiles of 4 waves (128x128
+  // per wave): one barrier per stage, in the middle (see below)
+  constexpr bool kMB = ((NW == 8 && BM == 256) || (NW == 4 && BM == 128) || (NW == 4 && BM == 256)) &&
+                       BN == 256 && !PART;
+  // 256x256 tiles of 4 waves (one per SIMD): a stage's DMA is split over its
+  // two k-steps, issued after the step's eight fragment reads (MFMAs 8-11)
+  constexpr bool kSplit = NW == 4 && BM == 256;
+  constexpr int kDmaAt = kSplit ? 8 : 0;  // MFMA after which a step's first DMA goes
   // stages of DMA issued before a tile's main loop
   constexpr int kPre = NS - 1;
   constexpr int kThreads = 64 * NW;
@@ -507,7 +522,8 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
                       u32x4 (&bn)[QN], int kt_rd, int step_rd, auto with_b, int kt_dma,
                       auto dma) {
         constexpr ReadOrder<QM, QN, decltype(with_b)::value> ord{};
-        static_assert(ord.n <= QM * QN && LPW <= QM * QN, "one read and one load per MFMA");
+        static_assert(ord.n <= QM * QN && kDmaAt + (kSplit ? LPW / 2 : LPW) <= QM * QN,
+                      "one read and one load per MFMA");
 #pragma unroll
         for (int q = 0; q < QM * QN; ++q) {
           const int i = q / QN, j = q % QN;
@@ -519,19 +535,25 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
             if (ord.kind[q] == 0) an[ord.idx[q]] = rd_a1(kt_rd, step_rd, ord.idx[q]);
             else rd_b1(kt_rd, step_rd, ord.idx[q], bn[ord.idx[q]]);
           }
-          if constexpr (decltype(dma)::value)
-            if (q < LPW) dma1(kt_dma, q);
+          if constexpr (decltype(dma)::value) {
+            constexpr int d0 = kSplit && decltype(dma)::half ? LPW / 2 : 0;
+            constexpr int nd = kSplit ? LPW / 2 : LPW;
+            if (q >= kDmaAt && q - kDmaAt < nd) dma1(kt_dma, d0 + q - kDmaAt);
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
       };
       // step 0 of stage kt (fp8: the B bytes of both steps came with step 0)
       auto step0 = [&](int kt, auto dma) {
-        step(aX, bX, aY, bY, kt, 1, std::integral_constant<bool, !F8>{}, kt + NS - 1, dma);
+        step(aX, bX, aY, bY, kt, 1, std::integral_constant<bool, !F8>{}, kt + NS - 1,
+             DmaTag<decltype(dma)::value, false>{});
       };
-      // step 1 of stage kt; at the last stage it reads a slot whose contents
-      // are not used
-      auto step1 = [&](int kt) {
-        step(aY, bY, aX, bX, kt + 1, 0, std::true_type{}, 0, std::false_type{});
+      // step 1 of stage kt (with a split stage, the second half of the DMA of
+      // stage kt + NS - 1: its slot was freed at the previous barrier); at the
+      // last stage it reads a slot whose contents are not used
+      auto step1 = [&](int kt, auto dma) {
+        step(aY, bY, aX, bX, kt + 1, 0, std::true_type{}, kt + NS - 1,
+             DmaTag<kSplit && decltype(dma)::value, true>{});
         if constexpr (F8) cvt_b(kt + 1);
       };
       wait_dma_and_barrier<LPW>(min(NS - 2, KT - 1));  // stage 0 visible
@@ -541,19 +563,21 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
       for (int j = 0; j < QN; ++j) rd_b1(0, 0, j, bX[j]);
       if constexpr (F8) cvt_b(0);
       // every stage but the last NS - 1 loads stage kt + NS - 1, so NS - 2
-      // later stages are in flight at each of these barriers
+      // later stages (NS - 2.5 with a split stage) are in flight at each of
+      // these barriers
       int kt = 0;
       for (; kt < KT - NS + 1; ++kt) {
         step0(kt, std::true_type{});
-        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((NS - 2) * LPW) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier"
+                     ::"n"((NS - 2) * LPW - (kSplit ? LPW / 2 : 0)) : "memory");
         __builtin_amdgcn_sched_barrier(0);
-        step1(kt);
+        step1(kt, std::true_type{});
       }
       for (; kt < KT; ++kt) {
         step0(kt, std::false_type{});
         wait_dma_and_barrier<LPW>(min(NS - 2, KT - 2 - kt));
         __builtin_amdgcn_sched_barrier(0);
-        step1(kt);
+        step1(kt, std::false_type{});
       }
     } else
     for (int kt = 0; kt < KT; ++kt) {
@@ -724,6 +748,13 @@ moe_status launch_dma_shape(const GroupedParams& p, int64_t max_routed_rows, hip
   const int groups = p.n_routed > 0 ? p.n_routed : 1;
   const bool small_tiles = p.t_dense == 0 && max_routed_rows / groups < kSmallRows;
   if (small_tiles) return launch_dma<BSRC, TL, EPI, 128, 256, 1, 4, 3, 2>(p, max_routed_rows, s);
+  // bf16 weights and no activation (the second expert GEMM): 4 waves of
+  // 128x128, which read a third less from LDS and hold a higher clock
+  // (prefill GEMM 2 3.24 -> 3.18 ms); with an activation epilogue, or fp8
+  // weights, 8 waves are faster (prefill GEMM 1 5.93 against 6.03 ms,
+  // DeepSeek-V3 GEMM 2 0.31 against 0.38 ms)
+  if constexpr (EPI == EPI_NONE && BSRC == B_SAME)
+    return launch_dma<BSRC, TL, EPI, 256, 256, 2, 2>(p, max_routed_rows, s);
   return launch_dma<BSRC, TL, EPI, 256, 256, 2, 4>(p, max_routed_rows, s);
 }
 
