@@ -718,24 +718,30 @@ __global__ void __launch_bounds__(256) topk_rows_kernel(
 // 32 tokens at a time; each wave runs v_mfma_f32_32x32x16_bf16 over a
 // quarter of d, with the tokens as M and up to 64 experts as N (one or two
 // 32-wide tiles; rows past E are zero).  x reaches the wave through its own
-// LDS ring by DMA (buffer_load ... lds, 16 token rows x 64 bytes per
-// instruction, the 16-byte chunks of row r placed at chunk c ^ h(r) so the
-// fragment reads are conflict-free); only the wave itself reads its ring,
-// so an s_waitcnt suffices, no barrier.  W_r (a few hundred KB at most,
-// L2-resident) is read straight into B fragments.  x blocks of 32 k and
-// their W_r fragments are loaded seven blocks ahead; the next tile's first
-// blocks are in flight while the current tile's partial logits are summed
-// through LDS (16 tokens at a time) and each token is selected by one
-// 16-lane row as in topk_rows_kernel.
+// LDS ring by DMA (buffer_load ... lds, 8 token rows x 128 bytes per
+// instruction: a cold read of the prefill input in this shape ran 8% faster
+// than in 16 rows x 64 bytes; the 16-byte chunks of row r are placed at
+// chunk c ^ h(r) so the fragment reads are conflict-free); only the wave
+// itself reads its ring, so an s_waitcnt suffices, no barrier.  W_r (a few
+// hundred KB at most, L2-resident) is read straight into B fragments.  x
+// blocks of 64 k and their W_r fragments are loaded three blocks ahead; the
+// next tile's first blocks are in flight while the current tile's partial
+// logits are summed through LDS (16 tokens at a time) and each token is
+// selected by one 16-lane row as in topk_rows_kernel.  The biases are
+// staged behind the first loads, not ahead of them.
 constexpr int kRmWaves = 4;
-constexpr int kRmRing = 8;          // x blocks per wave ring (seven ahead)
-constexpr int kRmBlock = 32 * 64;   // bytes of one block: 32 rows x 32 k
+constexpr int kRmRing = 4;           // x blocks per wave ring (three ahead)
+constexpr int kRmBlock = 32 * 128;   // bytes of one block: 32 rows x 64 k
+constexpr int kRmBlockK = kRmBlock / 64;
 
 __host__ __device__ constexpr size_t rm_lds_bytes(int E) {
   return (size_t)kRmWaves * kRmRing * kRmBlock + (size_t)(kRmWaves * 16 + 2) * E * sizeof(float);
 }
 
-__device__ __forceinline__ int rm_swz(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+// chunk slot of logical 16-byte chunk c of block row r is c ^ rm_swz(r):
+// any 8 consecutive rows, and the even (odd) rows of any 16, hit distinct
+// bank groups
+__device__ __forceinline__ int rm_swz(int r) { return ((r >> 1) ^ (r << 2)) & 7; }
 
 template <int NT>
 __global__ void __launch_bounds__(64 * kRmWaves, 2) route_mfma_kernel(
@@ -749,17 +755,20 @@ __global__ void __launch_bounds__(64 * kRmWaves, 2) route_mfma_kernel(
   float* part = reinterpret_cast<float*>(smem_raw + kRmWaves * kRmRing * kRmBlock);  // [w][16][E]
   float* s_brouter = part + kRmWaves * 16 * E;
   float* s_bselect = s_brouter + E;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    s_brouter[e] = b_router ? b_router[e] : 0.f;
-    s_bselect[e] = b_select ? b_select[e] : 0.f;
-  }
+  // the biases (E <= 64 < blockDim) are loaded now, written to LDS once the
+  // first x blocks are in flight, and read after the epilogue's barrier
+  const int eb = min((int)threadIdx.x, E - 1);
+  const float br_v = b_router ? b_router[eb] : 0.f;
+  const float bs_v = b_select ? b_select[eb] : 0.f;
+  __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the first x blocks
   const int h = lane >> 5;
   const int sub = lane & 15, row0 = lane & ~15;
-  const int nbw = d / 32 / kRmWaves;  // 32-k blocks of this wave's quarter of d
+  const int nbw = d / kRmBlockK / kRmWaves;  // 64-k blocks of this wave's quarter of d
   const int kb0 = wave * nbw;
   const int64_t tiles = (T_tok + 31) / 32;
-  // DMA lane role: row dr of the 16 of an instruction, logical chunk dc
-  const int dr = lane >> 2, dc = (lane & 3) ^ rm_swz(lane >> 2);
+  // DMA lane role: row dr of the 8 of an instruction; the chunk it loads
+  // depends on the instruction's rows through the swizzle
+  const int dr = lane >> 3;
   // B fragment rows: expert nt * 32 + (lane & 31), clamped (zeroed past E)
   const bf16_t* wrow[NT];
   bool bval[NT];
@@ -769,20 +778,25 @@ __global__ void __launch_bounds__(64 * kRmWaves, 2) route_mfma_kernel(
     bval[nt] = e < E;
     wrow[nt] = wr + (int64_t)min(e, E - 1) * d;
   }
-  u32x4 wb[kRmRing][NT][2];  // W_r fragments of the ring's blocks, both k-steps
-  // block blk (< nbw) of tile tl into ring slot `slot`: two DMA instructions
-  // (rows 0-15, 16-31; tokens past T re-read the last row) and the W_r
-  // fragments.  Exactly 2 + 2 NT vector-memory instructions.
+  constexpr int kSteps = kRmBlockK / 16;  // MFMA k-steps per block
+  constexpr int kDma = kRmBlock / 1024;    // DMA instructions per block
+  constexpr int kVm = kDma + kSteps * NT;  // vector-memory instructions per fetch
+  u32x4 wb[kRmRing][NT][kSteps];           // W_r fragments of the ring's blocks
+  // block blk (< nbw) of tile tl into ring slot `slot`: four DMA instructions
+  // (rows 8i .. 8i + 7; tokens past T re-read the last row) and the W_r
+  // fragments.  Exactly kVm vector-memory instructions.
   auto fetch = [&](int slot, int64_t tl, int blk) {
-    const int kk = (kb0 + blk) * 32;  // first k of the block
+    const int kk = (kb0 + blk) * kRmBlockK;  // first k of the block
     // the tile's 32 rows as a raw buffer (a buffer_load ... lds, unlike
     // global_load_lds, leaves the compiler's waits for the W_r registers
     // exact instead of waiting for every DMA in flight)
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(x + tl * 32 * d), 0, 32 * 2 * d, 0x00020000);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int64_t t = min(tl * 32 + 16 * i + dr, T_tok - 1);
+    for (int i = 0; i < kDma; ++i) {
+      const int r = 8 * i + dr;
+      const int dc = (lane & 7) ^ rm_swz(r);  // lane's LDS slot is lane & 7
+      const int64_t t = min(tl * 32 + r, T_tok - 1);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs, (void __attribute__((address_space(3)))*)(ring + slot * kRmBlock + i * 1024), 16,
           (int)((t - tl * 32) * 2 * d + (kk + dc * 8) * 2), 0, 0, 0);
@@ -790,13 +804,16 @@ __global__ void __launch_bounds__(64 * kRmWaves, 2) route_mfma_kernel(
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
-        wb[slot][nt][s] = *reinterpret_cast<const u32x4*>(wrow[nt] + kk + 8 * (2 * h + s));
+      for (int s = 0; s < kSteps; ++s)
+        wb[slot][nt][s] = *reinterpret_cast<const u32x4*>(wrow[nt] + kk + 8 * (2 * s + h));
   };
-  __syncthreads();  // biases staged
   int64_t tile = blockIdx.x;
 #pragma unroll
   for (int u = 0; u < kRmRing - 1; ++u) fetch(u, min(tile, tiles - 1), u);
+  if (threadIdx.x < E) {
+    s_brouter[threadIdx.x] = br_v;
+    s_bselect[threadIdx.x] = bs_v;
+  }
   for (; tile < tiles; tile += gridDim.x) {
     const int64_t next = min(tile + (int64_t)gridDim.x, tiles - 1);
     f32x16 acc[NT];
@@ -813,20 +830,28 @@ __global__ void __launch_bounds__(64 * kRmWaves, 2) route_mfma_kernel(
         fetch((u + kRmRing - 1) % kRmRing, here ? tile : next, here ? nb_ : nb_ - nbw);
         // slot u's DMA and fragments have landed: only the kRmRing - 1 later
         // fetches may be outstanding
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kRmRing - 1) * (2 + 2 * NT)) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kRmRing - 1) * kVm) : "memory");
         __builtin_amdgcn_sched_barrier(0);
         const unsigned char* st = ring + u * kRmBlock;
+        // all of the block's A fragments are read before its first MFMA (left
+        // alone the compiler waited out each read's latency before each MFMA);
+        // k-step s takes chunks 2s (lanes 0-31) and 2s + 1 (lanes 32-63)
+        u32x4 af[kSteps];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int r = lane & 31, c = 2 * h + s;  // A chunk: k [16h + 8s ... of the block order
-          const u32x4 af = *reinterpret_cast<const u32x4*>(st + r * 64 + ((c ^ rm_swz(r)) * 16));
+        for (int s = 0; s < kSteps; ++s) {
+          const int r = lane & 31, c = 2 * s + h;
+          af[s] = *reinterpret_cast<const u32x4*>(st + r * 128 + ((c ^ rm_swz(r)) * 16));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) {
             u32x4 bq = wb[u][nt][s];
             if (!bval[nt]) bq = u32x4{0, 0, 0, 0};
             acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8_t, af), __builtin_bit_cast(bf16x8_t, bq), acc[nt], 0, 0,
-                0);
+                __builtin_bit_cast(bf16x8_t, af[s]), __builtin_bit_cast(bf16x8_t, bq), acc[nt], 0,
+                0, 0);
           }
         }
         // the next refill overwrites the slot read here: keep it behind
@@ -949,7 +974,7 @@ bool mfma_rows_route(const moe_route_args* a) {
   // k-step, cost more than the logits GEMM + topk_rows_kernel path (Switch
   // workload: 43 against 41 us)
   return a->act_dtype == MOE_BF16 && a->E <= 32 && !grouped(a) &&
-         a->d % (32 * kRmWaves * kRmRing) == 0 && a->T > 1024;
+         a->d % (kRmBlockK * kRmWaves * kRmRing) == 0 && a->T > 1024;
 }
 
 bool mfma_route(const moe_route_args* a) {
