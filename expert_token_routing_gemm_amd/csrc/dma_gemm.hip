@@ -25,14 +25,16 @@
 //    the LDS-DMA costs ~17% (its writes contend with the fragment reads:
 //    the loop without global loads takes 5.35 instead of 6.4 ms on the
 //    prefill GEMM 1), and neither deeper prefetch nor one barrier per two
-//    stages helps.  4-wave 128x128 tiles (a third less LDS reading) are
-//    slower here: with one wave per SIMD its own LDS reads are not hidden.
+//    stages helps.  4-wave 128x128 tiles (a third less LDS reading) win
+//    only with the stage's DMA split over both k-steps and no activation
+//    epilogue (prefill GEMM 2 3.24 -> 3.18 ms; GEMM 1 6.03 against 5.93 ms).
 //  * 128x256 tiles (two workgroups per CU) run the same loop (Switch
 //    workload GEMM 1 351 -> 336 us); there the short K (1024) leaves the
 //    per-tile work (GELU epilogue, stores, pipeline refill) at ~45% of the
 //    time: without any loads in the loop GEMM 1 still takes 250 us.  The
-//    split-K router GEMM keeps one barrier at the top of each stage, the
-//    stage's fragments read, then its MFMAs.
+//    split-K router logits GEMM runs 256x256 tiles of 8 waves on this loop
+//    (DeepSeek-V3 share route 79.5 -> 74 us against 128x256 tiles of 4 waves
+//    with the older loop, one barrier at the top of each stage).
 //  * Every wave instruction fills 1 KB of LDS.  Row-major 16-bit operands:
 //    16 tile rows x 64 bytes, four consecutive lanes per row (full 64-byte
 //    global segments); inside the block the 16-byte chunks of row r are
@@ -119,22 +121,6 @@ __device__ __forceinline__ void store_c(bf16_t* p, float v) {
 #define MOE_GPTR(p) ((const void __attribute__((address_space(1)))*)(p))
 #define MOE_LPTR(p) ((void __attribute__((address_space(3)))*)(p))
 
-// Waits until the global_load_lds of this wave for the current stage are
-// done (at most `ahead` later stages of LPW loads each still in flight) and
-// the LDS reads of the previous stage have returned, then synchronises the
-// workgroup.
-template <int LPW>
-__device__ __forceinline__ void wait_stage_and_barrier(int ahead) {
-  static_assert(2 * LPW <= 63, "vmcnt range");
-  if (ahead >= 2) {
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * LPW) : "memory");
-  } else if (ahead == 1) {
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(LPW) : "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  }
-}
-
 // Waits until at most `stages` later stages of this wave's DMA (LPW
 // instructions each, 0 <= stages <= 3) are in flight and its LDS reads have
 // returned, then synchronises the workgroup.
@@ -190,8 +176,9 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
   // 256x256 tiles of 8 waves and 128x256 tiles of 4 waves (two workgroups
   // per CU), both 128x64 per wave, and 256x256 tiles of 4 waves (128x128
   // per wave): one barrier per stage, in the middle (see below)
-  constexpr bool kMB = ((NW == 8 && BM == 256) || (NW == 4 && BM == 128) || (NW == 4 && BM == 256)) &&
-                       BN == 256 && !PART;
+  static_assert(((NW == 8 && BM == 256) || (NW == 4 && BM == 128) || (NW == 4 && BM == 256)) &&
+                    BN == 256,
+                "tile shapes of the fenced schedule");
   // 256x256 tiles of 4 waves (one per SIMD): a stage's DMA is split over its
   // two k-steps, issued after the step's eight fragment reads (MFMAs 8-11)
   constexpr bool kSplit = NW == 4 && BM == 256;
@@ -436,7 +423,7 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
 #pragma unroll
         for (int r = 0; r < kScRegs; ++r) asm volatile("" ::"v"(cur.sr[j][r]));
     }
-    if constexpr (kMB) {
+    {
       // Two waves per SIMD (one workgroup of 8, or two of 4), 128x64 per
       // wave, one workgroup barrier per stage placed between the stage's two
       // 16-k steps.  The MFMAs of one step run while the fragments of the
@@ -579,70 +566,6 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
         __builtin_amdgcn_sched_barrier(0);
         step1(kt, std::false_type{});
       }
-    } else
-    for (int kt = 0; kt < KT; ++kt) {
-      float sc[QN];
-      if constexpr (F8) {
-        const int q = kt >> 2;  // 128-k block of this stage within the slice
-#pragma unroll
-        for (int j = 0; j < QN; ++j) {
-          float v = cur.sr[j][0];
-#pragma unroll
-          for (int r = 1; r < kScRegs; ++r)
-            if (q >= 64 * r) v = cur.sr[j][r];
-          sc[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), q & 63));
-        }
-      }
-      wait_stage_and_barrier<LPW>(min(NS - 2, KT - 1 - kt));
-      if (kt + NS - 1 < KT) issue(cur, kt + NS - 1);
-      const unsigned char* st = ring + (kt % NS) * STAGE_BYTES;
-      {
-        u32x4 bq[QN][2];  // B fragments of both k-steps
-#pragma unroll
-        for (int j = 0; j < QN; ++j) {
-          const int R = wn * WTN + j * 32 + (lane & 31);  // B tile row
-          if constexpr (F8) {
-            const int boff = TL ? ((R >> 4) & 1) * 512 + (16 * h + (R & 15)) * 16
-                                : (R & 31) * 32 + h * 16;
-            const u32x4 w8 = *reinterpret_cast<const u32x4*>(st + A_BYTES + (R >> 5) * 1024 + boff);
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-              for (int wv = 0; wv < 2; ++wv) {
-                const uint32_t word = w8[2 * s2 + wv];
-                typedef float f2_t __attribute__((ext_vector_type(2)));
-                const f2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
-                const f2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
-                bq[j][s2][2 * wv] = bf16_pair(lo.x * sc[j], lo.y * sc[j]);
-                bq[j][s2][2 * wv + 1] = bf16_pair(hi.x * sc[j], hi.y * sc[j]);
-              }
-            }
-          } else {
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-              const int c = 2 * h + s2, r = R & 15;
-              const int boff = TL ? (16 * c + r) * 16 : (r * 4 + (c ^ swz(r))) * 16;
-              bq[j][s2] = *reinterpret_cast<const u32x4*>(st + A_BYTES + (R >> 4) * 1024 + boff);
-            }
-          }
-        }
-#pragma unroll
-        for (int step = 0; step < BKE / 16; ++step) {
-          const int c = 2 * h + step;  // A chunk: k [16h + 8 step, +8)
-#pragma unroll
-          for (int i = 0; i < QM; ++i) {
-            const int R = wm * WTM + i * 32 + (lane & 31);  // A tile row
-            const int r = R & 15;
-            const u32x4 af =
-                *reinterpret_cast<const u32x4*>(st + (R >> 4) * 1024 + (r * 4 + (c ^ swz(r))) * 16);
-#pragma unroll
-            for (int j = 0; j < QN; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  __builtin_bit_cast(bf16x8_t, af), __builtin_bit_cast(bf16x8_t, bq[j][step]),
-                  acc[i][j], 0, 0, 0);
-          }
-        }
-      }
     }
 
     // every wave has finished reading the ring: start the next tile's loads
@@ -776,9 +699,9 @@ moe_status launch_dma_epi(int epi, const GroupedParams& p, int64_t max_routed_ro
 }  // namespace
 
 // Split-K fp32 partials for a single dense bf16 GEMM (the E >= 256 router
-// logits): 128x256 tiles, two workgroups per CU.
+// logits): 256x256 tiles of 8 waves, the fenced schedule of the expert GEMMs.
 moe_status launch_dma_partial(const GroupedParams& p, hipStream_t stream) {
-  return launch_dma<B_SAME, false, EPI_NONE, 128, 256, 1, 4, 3, 2, true>(p, 0, stream);
+  return launch_dma<B_SAME, false, EPI_NONE, 256, 256, 2, 4, 4, 1, true>(p, 0, stream);
 }
 
 // bf16 or fp8 weights (row-major or tiled); output columns in whole 256-wide

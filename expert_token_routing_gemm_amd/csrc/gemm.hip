@@ -581,19 +581,19 @@ moe_status run_ffn(const moe_ffn_args* a, const FfnPlan& pl, void* ws, hipStream
 
 }  // namespace
 
-// Split-K slices for the router GEMM on the LDS-DMA kernel (E a multiple of
-// 256: whole 256-wide tiles): enough 128-row x slice work items for two
-// workgroups per CU.
-// K slices of the router logits GEMM: enough (tile, slice) work items for
-// kLogitsWgPerCu per CU, at most kLogitsMaxKs.  Each slice writes
-// and re-reads T x E fp32 partials, so more slices are not free: on the
-// DeepSeek-V3 share (T = 8192, E = 256) 4 slices (one item per CU) route in
-// 77 us, 8 slices (two per CU) in 85 us, 2 slices in 101 us.
+// K slices of the router logits GEMM on the LDS-DMA kernel (E a multiple
+// of 256: whole 256-wide tiles; 256-row tiles): enough (tile, slice) work
+// items for kLogitsWgPerCu per CU, at most kLogitsMaxKs.  Each slice writes
+// and re-reads T x E fp32 partials, so more slices are not free.  On the
+// DeepSeek-V3 share (T = 8192, E = 256, cache-cold) 8 slices of 256-row
+// tiles (one item per CU, two waves per SIMD) route in 74 us; 128-row tiles
+// of 4 waves took 79-80 us with 4 slices (one item per CU) whether their
+// ring held 3, 5 or 6 stages, and 81 us with 8 slices (two per CU).
 constexpr int kLogitsWgPerCu = 1;
 constexpr int kLogitsMaxKs = 16;
 int dense_logits_ksplit(int64_t T, int d, int E) {
   if (E % 256 != 0 || d % BKE_DMA != 0) return 1;
-  const int64_t m_tiles = (T + 127) / 128;
+  const int64_t m_tiles = (T + 255) / 256;
   const int64_t target = kLogitsWgPerCu * (int64_t)device_info().cus;
   int ks = 1;
   while (ks < kLogitsMaxKs && m_tiles * ks < target && (d / BKE_DMA) % (2 * ks) == 0) ks *= 2;

@@ -12,7 +12,7 @@
 //   route_mfma_kernel  : bf16, E <= 32, many tokens.  Logits on the matrix
 //                        cores (x by DMA through per-wave LDS rings), top-k
 //                        and weights fused.  Measured on the prefill workload
-//                        (E = 8, d = 4096): 37 us, against 70 us for the
+//                        (E = 8, d = 4096): 31 us cache-cold, against 70 us for the
 //                        VALU kernel below, whose FMAs and bf16 widening
 //                        limited it well below the HBM rate.
 //   route_small_kernel : E <= 8 and W_r fits in LDS (fp32, or few tokens).
@@ -713,11 +713,11 @@ __global__ void __launch_bounds__(256) topk_rows_kernel(
   }
 }
 
-// ---------------------------------------------------------------- E <= 64, bf16, many tokens
+// ---------------------------------------------------------------- E <= 32, bf16, many tokens
 // Logits on the matrix cores, top-k fused.  A workgroup of four waves takes
 // 32 tokens at a time; each wave runs v_mfma_f32_32x32x16_bf16 over a
-// quarter of d, with the tokens as M and up to 64 experts as N (one or two
-// 32-wide tiles; rows past E are zero).  x reaches the wave through its own
+// quarter of d, with the tokens as M and the experts as N (one 32-wide
+// tile; columns past E are computed from row E - 1 of W_r and dropped).  x reaches the wave through its own
 // LDS ring by DMA (buffer_load ... lds, 8 token rows x 128 bytes per
 // instruction: a cold read of the prefill input in this shape ran 8% faster
 // than in 16 rows x 64 bytes; the 16-byte chunks of row r are placed at
@@ -769,15 +769,11 @@ __global__ void __launch_bounds__(64 * kRmWaves, 2) route_mfma_kernel(
   // DMA lane role: row dr of the 8 of an instruction; the chunk it loads
   // depends on the instruction's rows through the swizzle
   const int dr = lane >> 3;
-  // B fragment rows: expert nt * 32 + (lane & 31), clamped (zeroed past E)
+  // B fragment rows: expert nt * 32 + (lane & 31), clamped to E - 1; a
+  // column past E only ever feeds its own logits column, which is never read
   const bf16_t* wrow[NT];
-  bool bval[NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int e = nt * 32 + (lane & 31);
-    bval[nt] = e < E;
-    wrow[nt] = wr + (int64_t)min(e, E - 1) * d;
-  }
+  for (int nt = 0; nt < NT; ++nt) wrow[nt] = wr + (int64_t)min(nt * 32 + (lane & 31), E - 1) * d;
   constexpr int kSteps = kRmBlockK / 16;  // MFMA k-steps per block
   constexpr int kDma = kRmBlock / 1024;    // DMA instructions per block
   constexpr int kVm = kDma + kSteps * NT;  // vector-memory instructions per fetch
@@ -792,14 +788,14 @@ __global__ void __launch_bounds__(64 * kRmWaves, 2) route_mfma_kernel(
     // exact instead of waiting for every DMA in flight)
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(x + tl * 32 * d), 0, 32 * 2 * d, 0x00020000);
+    const int rlast = (int)min(T_tok - 1 - tl * 32, (int64_t)31);  // last row of the tile
 #pragma unroll
     for (int i = 0; i < kDma; ++i) {
       const int r = 8 * i + dr;
       const int dc = (lane & 7) ^ rm_swz(r);  // lane's LDS slot is lane & 7
-      const int64_t t = min(tl * 32 + r, T_tok - 1);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rs, (void __attribute__((address_space(3)))*)(ring + slot * kRmBlock + i * 1024), 16,
-          (int)((t - tl * 32) * 2 * d + (kk + dc * 8) * 2), 0, 0, 0);
+          min(r, rlast) * 2 * d + (kk + dc * 8) * 2, 0, 0, 0);
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
@@ -847,11 +843,9 @@ __global__ void __launch_bounds__(64 * kRmWaves, 2) route_mfma_kernel(
         for (int s = 0; s < kSteps; ++s) {
 #pragma unroll
           for (int nt = 0; nt < NT; ++nt) {
-            u32x4 bq = wb[u][nt][s];
-            if (!bval[nt]) bq = u32x4{0, 0, 0, 0};
             acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8_t, af[s]), __builtin_bit_cast(bf16x8_t, bq), acc[nt], 0,
-                0, 0);
+                __builtin_bit_cast(bf16x8_t, af[s]), __builtin_bit_cast(bf16x8_t, wb[u][nt][s]),
+                acc[nt], 0, 0, 0);
           }
         }
         // the next refill overwrites the slot read here: keep it behind
@@ -967,12 +961,11 @@ bool small_route_fits(const moe_route_args* a) {
 }
 
 
-// bf16, E <= 64 without group limits, many tokens: route_mfma_kernel
+// bf16, E <= 32 without group limits, many tokens: route_mfma_kernel
 bool mfma_rows_route(const moe_route_args* a) {
-  // each wave's quarter of d is a whole number of ring rounds of 32-k blocks.
-  // E <= 32 only: at E = 64 the B fragments, two 32-row gathers from W_r per
-  // k-step, cost more than the logits GEMM + topk_rows_kernel path (Switch
-  // workload: 43 against 41 us)
+  // each wave's quarter of d is a whole number of ring rounds of 64-k blocks.
+  // E <= 32 only: with two 32-wide expert tiles the ring's W_r fragments
+  // (128 registers) no longer fit two workgroups per CU without spilling
   return a->act_dtype == MOE_BF16 && a->E <= 32 && !grouped(a) &&
          a->d % (kRmBlockK * kRmWaves * kRmRing) == 0 && a->T > 1024;
 }
