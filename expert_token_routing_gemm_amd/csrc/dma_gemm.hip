@@ -11,10 +11,12 @@
 //    activation use 4 waves of 128x128 (256 accumulators per lane in
 //    AccVGPRs, one wave per SIMD), each stage's DMA split over its two
 //    k-steps.  Groups averaging a few hundred rows (with no shared expert)
-//    use 128x256 tiles of 4 waves, two workgroups per CU.
+//    use 128x256 tiles of 4 waves, two workgroups per CU, or, without an
+//    activation and with whole 512-column tiles, 128x512 tiles of 8 waves
+//    (128x64 each), one workgroup per CU.
 //  * Global -> LDS with global_load_lds_dwordx4 (no register staging) into
 //    a ring of 32-k stages: 4 stages of 32 KB (24 KB with fp8 weights) for
-//    256x256 tiles, 3 for 128x256.  Each wave waits for its own loads of a
+//    256x256 tiles, 3 for 128x256 and 128x512.  Each wave waits for its own loads of a
 //    stage (vmcnt), then a workgroup barrier makes them visible; the
 //    compiler does not track these waits, they are issued explicitly.
 //  * 256x256 main loop: one barrier per stage, between its two 16-k steps.
@@ -173,11 +175,13 @@ template <int BSRC, bool TL, int EPI, int BM, int BN, int WM_, int WN_, int NS, 
 __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedParams p) {
   constexpr bool F8 = BSRC == B_FP8;
   constexpr int NW = WM_ * WN_;                  // waves
-  // 256x256 tiles of 8 waves and 128x256 tiles of 4 waves (two workgroups
-  // per CU), both 128x64 per wave, and 256x256 tiles of 4 waves (128x128
-  // per wave): one barrier per stage, in the middle (see below)
-  static_assert(((NW == 8 && BM == 256) || (NW == 4 && BM == 128) || (NW == 4 && BM == 256)) &&
-                    BN == 256,
+  // 256x256 tiles of 8 waves, 128x256 tiles of 4 waves (two workgroups per
+  // CU) and 128x512 tiles of 8 waves, all 128x64 per wave, and 256x256 tiles
+  // of 4 waves (128x128 per wave): one barrier per stage, in the middle (see
+  // below)
+  static_assert((((NW == 8 && BM == 256) || (NW == 4 && BM == 128) || (NW == 4 && BM == 256)) &&
+                 BN == 256) ||
+                    (NW == 8 && BM == 128 && BN == 512),
                 "tile shapes of the fenced schedule");
   // 256x256 tiles of 4 waves (one per SIMD): a stage's DMA is split over its
   // two k-steps, issued after the step's eight fragment reads (MFMAs 8-11)
@@ -670,6 +674,13 @@ template <int BSRC, bool TL, int EPI>
 moe_status launch_dma_shape(const GroupedParams& p, int64_t max_routed_rows, hipStream_t s) {
   const int groups = p.n_routed > 0 ? p.n_routed : 1;
   const bool small_tiles = p.t_dense == 0 && max_routed_rows / groups < kSmallRows;
+  // Without an activation epilogue, 128x512 tiles of 8 waves: a sixth fewer
+  // bytes per flop through the LDS DMA, which bounds these tiles (Switch
+  // GEMM 2 273 -> 253 us); with one, the two 128x256 workgroups of a CU
+  // overlap one's epilogue with the other's main loop (Switch GEMM 1 286 us
+  // against 290-295 us on 128x512 tiles).
+  if (EPI == EPI_NONE && small_tiles && p.N % 512 == 0)
+    return launch_dma<BSRC, TL, EPI, 128, 512, 1, 8, 3, 1>(p, max_routed_rows, s);
   if (small_tiles) return launch_dma<BSRC, TL, EPI, 128, 256, 1, 4, 3, 2>(p, max_routed_rows, s);
   // bf16 weights and no activation (the second expert GEMM): 4 waves of
   // 128x128, which read a third less from LDS and hold a higher clock
