@@ -10,20 +10,22 @@
 // buffer-management bullet), which also fixes which assignments are dropped:
 // the ones past the first C in token-major order.
 //
-// Large batches: three kernels, no ordering atomics (results are
+// Large batches: two kernels, no ordering atomics (results are
 // deterministic); small and tiny batches: see below.
 //   hist_kernel      : block b owns a chunk of TB tokens (TB*k <= 256
-//                      assignments); LDS-private histogram -> blk[b][e].
-//   scan_kernel      : one workgroup; per expert an exclusive scan over blocks
-//                      (blk -> base, split over kScanThreads / E chunks), counts,
-//                      kept = min(counts, C), the expert offsets by a
-//                      wave-level scan, per-rank counts.
-//   rank_pack_kernel : recomputes each assignment's position: block base +
-//                      earlier waves of the block + lanes of its wave holding
-//                      the same expert (ballot / popcount), which is exactly
-//                      the token-major position.  Writes slot and src, then
-//                      copies each token's row once from x into its kept slots
-//                      with 128-bit loads and stores (x is read once).
+//                      assignments); LDS-private histogram -> blk[b][e] (rows
+//                      padded to a multiple of 4 experts with zeros).
+//   rank_pack_kernel : every block first sums the column of each expert over
+//                      all blocks (the total) and over the blocks before its
+//                      own (its base), then kept = min(total, C) and the
+//                      expert offsets by a wave-level scan; block 0 writes the
+//                      counts, offsets and per-rank counts.  Each assignment's
+//                      position is block base + earlier waves of the block +
+//                      lanes of its wave holding the same expert (ballot /
+//                      popcount), which is exactly the token-major position.
+//                      Writes slot and src, then copies each token's row once
+//                      from x into its kept slots with 128-bit loads and
+//                      stores (x is read once).
 #include "common.h"
 
 namespace moe {
@@ -43,7 +45,8 @@ __global__ void __launch_bounds__(kThreads) hist_kernel(const int32_t* __restric
                                                        int32_t* __restrict__ blk, int64_t n_assign,
                                                        int per_block, int E) {
   __shared__ int cnt[MOE_MAX_EXPERTS];
-  for (int e = threadIdx.x; e < E; e += kThreads) cnt[e] = 0;
+  const int E4 = (E + 3) & ~3;  // row stride of blk
+  for (int e = threadIdx.x; e < E4; e += kThreads) cnt[e] = 0;
   __syncthreads();
   const int64_t g = (int64_t)blockIdx.x * per_block + threadIdx.x;
   if (threadIdx.x < per_block && g < n_assign) {
@@ -51,128 +54,124 @@ __global__ void __launch_bounds__(kThreads) hist_kernel(const int32_t* __restric
     if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);  // ids outside [0, E) are ignored
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kThreads) blk[(int64_t)blockIdx.x * E + e] = cnt[e];
+  for (int e = threadIdx.x; e < E4; e += kThreads) blk[(int64_t)blockIdx.x * E4 + e] = cnt[e];
 }
 
-// scan_kernel: one workgroup of kScanThreads.  Thread (p, e) = (tid / E,
-// tid % E) owns expert e on the p-th of P = kScanThreads / E contiguous
-// block chunks, so the lanes of a wave read consecutive experts of a block
-// (coalesced).  Chunk sums meet in LDS, each thread adds the sums of the
-// earlier chunks of its expert, and a second pass writes every block's
-// exclusive base (to a separate array, so all loads of a pass are
-// independent and G of them are in flight per thread).
-constexpr int kScanThreads = 1024;
-
-__global__ void __launch_bounds__(kScanThreads) scan_kernel(
-    const int32_t* __restrict__ blk, int32_t* __restrict__ base, int nblocks, int E, int R, int C,
-    int32_t* __restrict__ counts, int32_t* __restrict__ kept, int32_t* __restrict__ off,
-    int32_t* __restrict__ rank_counts, int32_t* __restrict__ rank_off) {
-  constexpr int G = 32;  // independent loads in flight per thread
-  __shared__ int part[kScanThreads];  // [P][E] chunk sums
-  __shared__ int tot[MOE_MAX_EXPERTS];
-  __shared__ int wsum[MOE_MAX_EXPERTS / 64];
-  __shared__ int sh_off[MOE_MAX_EXPERTS + 1];
-  const int tid = threadIdx.x;
-  const int lane = lane_id();
-  const int P = kScanThreads / E;
-  const int e = tid % E;
-  const int p = tid / E;
-  const bool active = p < P;
-  const int chunk = (nblocks + P - 1) / P;
-  const int b0 = min(p * chunk, nblocks);
-  const int b1 = active ? min(b0 + chunk, nblocks) : b0;
-  int sum = 0;
-  {
-    int b = b0;
-    for (; b + G <= b1; b += G) {
-      int v[G];
-#pragma unroll
-      for (int i = 0; i < G; ++i) v[i] = blk[(int64_t)(b + i) * E + e];
-#pragma unroll
-      for (int i = 0; i < G; ++i) sum += v[i];
-    }
-    for (; b < b1; ++b) sum += blk[(int64_t)b * E + e];
-  }
-  if (active) part[p * E + e] = sum;
-  __syncthreads();
-  if (active) {
-    int run = 0;
-    for (int q = 0; q < p; ++q) run += part[q * E + e];
-    if (p == P - 1) tot[e] = run + sum;
-    int b = b0;
-    for (; b + G <= b1; b += G) {
-      int v[G];
-#pragma unroll
-      for (int i = 0; i < G; ++i) v[i] = blk[(int64_t)(b + i) * E + e];
-#pragma unroll
-      for (int i = 0; i < G; ++i) {
-        base[(int64_t)(b + i) * E + e] = run;
-        run += v[i];
-      }
-    }
-    for (; b < b1; ++b) {
-      const int v = blk[(int64_t)b * E + e];
-      base[(int64_t)b * E + e] = run;
-      run += v;
-    }
-  }
-  __syncthreads();
-  // exclusive scan of kept over the experts (threads 0..255)
-  int kp = 0, ex = 0;
-  if (tid < MOE_MAX_EXPERTS) {
-    kp = tid < E ? min(tot[tid], C) : 0;
-    ex = kp;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int u = __shfl_up(ex, o, 64);
-      if (lane >= o) ex += u;
-    }
-    if (lane == 63) wsum[tid / 64] = ex;
-  }
-  __syncthreads();
-  if (tid < E) {
-    for (int i = 0; i < tid / 64; ++i) ex += wsum[i];
-    counts[tid] = tot[tid];
-    kept[tid] = kp;
-    off[tid] = ex - kp;
-    sh_off[tid] = ex - kp;
-    if (tid == E - 1) {
-      off[E] = ex;
-      sh_off[E] = ex;
-    }
-  }
-  __syncthreads();
-  const int per = E / R;
-  for (int r = tid; r < R; r += kScanThreads) {
-    rank_counts[r] = sh_off[(r + 1) * per] - sh_off[r * per];
-    rank_off[r] = sh_off[r * per];
-  }
-  if (tid == 0) rank_off[R] = sh_off[E];
-}
+// Chunks of blocks the preamble of rank_pack_kernel splits the columns of
+// blk into (at most): each thread sums one chunk of one 4-expert column
+// with 16-byte loads, and every expert then adds up to this many partial
+// sums.
+constexpr int kPreChunks = 16;
 
 template <int UNROLL>
 __global__ void __launch_bounds__(kThreads) rank_pack_kernel(
-    const int32_t* __restrict__ ids, const int32_t* __restrict__ blk_base,
-    const int32_t* __restrict__ off, const u32x4* __restrict__ x, int32_t* __restrict__ slot_out,
-    int32_t* __restrict__ src_out, u32x4* __restrict__ x_send, int64_t T, int k, int E, int C,
-    int tokens_per_block, int row16) {
-  __shared__ int wcnt[kWaves][MOE_MAX_EXPERTS];
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ blk, int nblocks,
+    const u32x4* __restrict__ x, int32_t* __restrict__ slot_out, int32_t* __restrict__ src_out,
+    u32x4* __restrict__ x_send, int64_t T, int k, int E, int R, int C, int tokens_per_block,
+    int row16, int32_t* __restrict__ counts, int32_t* __restrict__ kept_out,
+    int32_t* __restrict__ off_out, int32_t* __restrict__ rank_counts,
+    int32_t* __restrict__ rank_off) {
+  __shared__ int wcnt[kWaves][MOE_MAX_EXPERTS];   // wave counts, then wave bases
+  __shared__ int base[MOE_MAX_EXPERTS];           // this block's base per expert
   __shared__ int sl[kThreads];
+  __shared__ int4 pre_part[kThreads];  // [chunk][4-expert column]
+  __shared__ int4 tot_part[kThreads];
+  __shared__ int s_off[MOE_MAX_EXPERTS + 1];
+  __shared__ int s_wsum[kWaves];
   const int lane = lane_id();
   const int w = threadIdx.x / 64;
   const int per_block = tokens_per_block * k;
   const int64_t n_assign = T * k;
   for (int i = threadIdx.x; i < kWaves * MOE_MAX_EXPERTS; i += kThreads) (&wcnt[0][0])[i] = 0;
-  __syncthreads();
+  // this thread's assignment, loaded before the preamble's loads
   const int64_t g = (int64_t)blockIdx.x * per_block + threadIdx.x;
   const bool in_range = threadIdx.x < per_block && g < n_assign;
   const int e = in_range ? ids[g] : -1;
   const bool valid = in_range && e >= 0 && e < E;
+
+  // Preamble: the totals of every expert over all blocks and its base
+  // (the assignments of the blocks before this one).  Thread (p, q) sums
+  // 4-expert column q over block chunk p with 16-byte loads, all issued
+  // before any is used.
+  {
+    const int Q = (E + 3) >> 2;  // 4-expert columns of blk
+    const int P = min(kThreads / Q, kPreChunks);
+    const int q = threadIdx.x % Q, p = threadIdx.x / Q;
+    if (p < P) {
+      const int chunk = (nblocks + P - 1) / P;
+      const int r0 = min(p * chunk, nblocks), r1 = min(r0 + chunk, nblocks);
+      const int4* col = reinterpret_cast<const int4*>(blk) + q;
+      int4 tot = {0, 0, 0, 0}, pre = {0, 0, 0, 0};
+      const int b = (int)blockIdx.x;
+      int r = r0;
+      for (; r + 16 <= r1; r += 16) {
+        int4 v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = col[(int64_t)(r + i) * Q];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          tot.x += v[i].x; tot.y += v[i].y; tot.z += v[i].z; tot.w += v[i].w;
+          if (r + i < b) { pre.x += v[i].x; pre.y += v[i].y; pre.z += v[i].z; pre.w += v[i].w; }
+        }
+      }
+      for (; r < r1; ++r) {
+        const int4 v = col[(int64_t)r * Q];
+        tot.x += v.x; tot.y += v.y; tot.z += v.z; tot.w += v.w;
+        if (r < b) { pre.x += v.x; pre.y += v.y; pre.z += v.z; pre.w += v.w; }
+      }
+      pre_part[p * Q + q] = pre;
+      tot_part[p * Q + q] = tot;
+    }
+    __syncthreads();
+    // expert e = thread: total, base, kept; exclusive scan of kept over the
+    // experts (a wave scan, then the sums of earlier waves)
+    int tot = 0, pre = 0;
+    if ((int)threadIdx.x < E) {
+      const int xe = threadIdx.x;
+      for (int pp = 0; pp < P; ++pp) {
+        tot += reinterpret_cast<const int*>(&tot_part[pp * Q + (xe >> 2)])[xe & 3];
+        pre += reinterpret_cast<const int*>(&pre_part[pp * Q + (xe >> 2)])[xe & 3];
+      }
+    }
+    const int kp = (int)threadIdx.x < E ? min(tot, C) : 0;
+    int ex = kp;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(ex, o, 64);
+      if (lane >= o) ex += u;
+    }
+    if (lane == 63) s_wsum[w] = ex;
+    __syncthreads();
+    for (int i = 0; i < w; ++i) ex += s_wsum[i];
+    if ((int)threadIdx.x < E) {
+      const int xe = threadIdx.x;
+      s_off[xe] = ex - kp;
+      base[xe] = pre;
+      if (xe == E - 1) s_off[E] = ex;
+      if (blockIdx.x == 0) {
+        counts[xe] = tot;
+        kept_out[xe] = kp;
+        off_out[xe] = ex - kp;
+        if (xe == E - 1) off_out[E] = ex;
+      }
+    }
+    __syncthreads();
+    if (blockIdx.x == 0) {
+      const int per = E / R;
+      for (int rr = threadIdx.x; rr < R; rr += kThreads) {
+        rank_counts[rr] = s_off[(rr + 1) * per] - s_off[rr * per];
+        rank_off[rr] = s_off[rr * per];
+      }
+      if (threadIdx.x == 0) rank_off[R] = s_off[E];
+    }
+  }
+
+  // wave counts of this block
   if (valid) atomicAdd(&wcnt[w][e], 1);
   __syncthreads();
   // per-wave bases: block base + counts of the earlier waves
   for (int ee = threadIdx.x; ee < E; ee += kThreads) {
-    int run = blk_base[(int64_t)blockIdx.x * E + ee];
+    int run = base[ee];
 #pragma unroll
     for (int i = 0; i < kWaves; ++i) {
       const int c = wcnt[i][ee];
@@ -195,7 +194,7 @@ __global__ void __launch_bounds__(kThreads) rank_pack_kernel(
   if (valid) {
     const int pos = wcnt[w][e] + r;
     if (pos < C) {
-      s = off[e] + pos;
+      s = s_off[e] + pos;
       src_out[s] = (int32_t)(g / k);
     }
   }
@@ -559,7 +558,8 @@ extern "C" int64_t moe_send_rows_max(int64_t T, int32_t k, int32_t E, int32_t ca
 extern "C" size_t moe_dispatch_workspace_bytes(const moe_dispatch_args* a) {
   if (!a || a->T <= 0 || a->k <= 0 || a->T * a->k <= kSmallAssign) return 0;
   const Plan p = plan_for(a->T, a->k);
-  return 2 * align_up((size_t)p.nblocks * a->E * sizeof(int32_t), 256);
+  const int E4 = (a->E + 3) & ~3;  // block histogram rows padded to 4 experts
+  return align_up((size_t)p.nblocks * E4 * sizeof(int32_t), 256);
 }
 
 extern "C" moe_status moe_dispatch(const moe_dispatch_args* a, void* ws, size_t ws_bytes,
@@ -605,21 +605,17 @@ extern "C" moe_status moe_dispatch(const moe_dispatch_args* a, void* ws, size_t 
     return MOE_OK;
   }
   int32_t* blk = static_cast<int32_t*>(ws);
-  int32_t* bases = blk + align_up((size_t)p.nblocks * a->E * sizeof(int32_t), 256) / sizeof(int32_t);
-  if (a->T > 0) {
-    hist_kernel<<<p.nblocks, kThreads, 0, stream>>>(a->ids, blk, a->T * a->k,
-                                                     p.tokens_per_block * a->k, a->E);
+  const int nblocks = a->T > 0 ? p.nblocks : 0;
+  if (nblocks > 0) {
+    hist_kernel<<<nblocks, kThreads, 0, stream>>>(a->ids, blk, a->T * a->k,
+                                                  p.tokens_per_block * a->k, a->E);
     MOE_CHECK_LAUNCH();
   }
-  scan_kernel<<<1, kScanThreads, 0, stream>>>(blk, bases, a->T > 0 ? p.nblocks : 0, a->E, a->R,
-                                              a->capacity, a->counts, a->kept, a->expert_off,
-                                              a->rank_counts, a->rank_off);
+  // with no tokens one block still writes the zero counts and offsets
+  rank_pack_kernel<4><<<nblocks > 0 ? nblocks : 1, kThreads, 0, stream>>>(
+      a->ids, blk, nblocks, (const u32x4*)a->x, a->slot, a->src, (u32x4*)a->x_send, a->T, a->k,
+      a->E, a->R, a->capacity, p.tokens_per_block, row16, a->counts, a->kept, a->expert_off,
+      a->rank_counts, a->rank_off);
   MOE_CHECK_LAUNCH();
-  if (a->T > 0) {
-    rank_pack_kernel<4><<<p.nblocks, kThreads, 0, stream>>>(
-        a->ids, bases, a->expert_off, (const u32x4*)a->x, a->slot, a->src, (u32x4*)a->x_send, a->T,
-        a->k, a->E, a->capacity, p.tokens_per_block, row16);
-    MOE_CHECK_LAUNCH();
-  }
   return MOE_OK;
 }
