@@ -207,7 +207,7 @@ __global__ void __launch_bounds__(64 * WM_ * WN_, MINW) dma_gemm_kernel(GroupedP
   int* s_tstart = reinterpret_cast<int*>(smem + NS * STAGE_BYTES);
   int* s_rows = s_tstart + (kMaxGroups + 1);
   int* s_r0 = s_rows + kMaxGroups;
-  int* s_scan = s_r0 + kMaxGroups;
+  int* s_scan = s_r0 + kMaxGroups;  // [8]: one partial sum per wave of the preamble's scan
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -644,7 +644,7 @@ moe_status launch_dma(const GroupedParams& p, int64_t max_routed_rows, hipStream
   auto kern = dma_gemm_kernel<BSRC, TL, EPI, BM, BN, WM_, WN_, NS, MINW, PART>;
   constexpr int per_cu = MINW * 4 / (WM_ * WN_) > 0 ? MINW * 4 / (WM_ * WN_) : 1;  // workgroups
   constexpr size_t lds = NS * (BM * 2 + BN * (BSRC == B_FP8 ? 1 : 2)) * BKE +
-                         (3 * kMaxGroups + 1 + 4) * sizeof(int);
+                         (3 * kMaxGroups + 1 + 8) * sizeof(int);
   static_assert(per_cu * lds <= 160 * 1024, "LDS of the resident workgroups");
   MOE_CHECK_HIP(set_dynamic_lds((const void*)kern, (int)lds));
   const int nt = p.N / BN;
