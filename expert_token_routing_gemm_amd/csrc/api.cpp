@@ -2,8 +2,8 @@
 // whole-layer entry point and its workspace.
 #include <string.h>
 
+#include <map>
 #include <mutex>
-#include <set>
 #include <utility>
 #include <vector>
 
@@ -49,15 +49,19 @@ DeviceInfo device_info() {
 }
 
 hipError_t set_dynamic_lds(const void* kernel, int bytes) {
+  // the largest size set so far per (device, kernel): a kernel whose LDS
+  // depends on its arguments (the router's on E) is raised when a call
+  // needs more than any before it
   static std::mutex mu;
-  static std::set<std::pair<int, const void*>> done;
+  static std::map<std::pair<int, const void*>, int> done;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   std::lock_guard<std::mutex> lock(mu);
-  if (done.count({dev, kernel})) return hipSuccess;
+  auto it = done.find({dev, kernel});
+  if (it != done.end() && it->second >= bytes) return hipSuccess;
   e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e == hipSuccess) done.insert({dev, kernel});
+  if (e == hipSuccess) done[{dev, kernel}] = bytes;
   return e;
 }
 

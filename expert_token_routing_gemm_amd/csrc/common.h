@@ -56,7 +56,8 @@ struct DeviceInfo {
 DeviceInfo device_info();
 
 // Allows `kernel` `bytes` of dynamic LDS on the current device; the attribute
-// is set once per (device, kernel) and the call is thread-safe.
+// is set again only when a call asks for more than before on that device,
+// and the call is thread-safe.
 hipError_t set_dynamic_lds(const void* kernel, int bytes);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
