@@ -5,7 +5,9 @@ over one batch of seeded synthetic input, inputs resident in HBM.  Default
 workload: the prefill-shaped Mixtral-style bf16 layer (T=16384 tokens,
 d=4096, 8 SwiGLU experts with h=14336, top-2, softmax renormalised, skewed
 logit offsets, no drops), the largest of the five workloads by flops and
-bytes; ``--config i`` selects another.
+bytes; ``--config i`` selects another.  Without ``--config``, the line also
+carries the other four workloads under ``other_workloads`` (tokens/s and the
+first expert GEMM against its roofline, timed the same way on fewer steps).
 
 Prints one JSON line: tokens/s over the timed steps (back to back), the
 roofline of the dominant kernel (the first expert GEMM) from HIP events
@@ -41,6 +43,7 @@ TRAFFIC_RECORDS = {0: "profiles/gemm1_snippet_traffic.json",
                    3: "profiles/gemm1_switch_traffic.json",
                    4: "profiles/gemm1_deepseek_traffic.json"}
 MALL_FLUSH_MIB = 512           # > 2x the 256 MB Infinity Cache
+DEFAULT_CONFIG = 2             # the prefill-shaped Mixtral layer: the largest workload
 STAGES = ["route", "dispatch", "gemm1", "gemm2", "combine"]
 
 
@@ -267,13 +270,95 @@ def dense_reference(wl, steps: int):
                       "tflops": 2.0 * M * N * K / ms / 1e9}), flush=True)
 
 
+def timed_steps(layer, K: int, W: int, hip):
+    """W untimed forwards, then K timed back to back between synchronises;
+    only the two events around the first expert GEMM are recorded (each
+    recorded event delays the next kernel by a few microseconds): they give
+    the dominant kernel's duration per step.  Returns (wall s, GEMM 1 ms)."""
+    import numpy as np
+    import torch
+    for _ in range(W):
+        layer.forward()
+    torch.cuda.synchronize()
+    ev = Events(hip, 2 * K)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        layer.forward(events=[None, None, ev.ev[2 * s], ev.ev[2 * s + 1], None, None])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gemm1_ms = float(np.mean([ev.ms(2 * s, 2 * s + 1) for s in range(K)]))
+    ev.close()
+    return wall, gemm1_ms
+
+
+def dominant_roofline(wl, cfg: int, gemm1_ms: float, nbytes, flops, w_layout: str):
+    """The first expert GEMM against its roofline: HBM for the decode
+    workload (it streams w1 and w3), the matrix cores otherwise."""
+    g1_s = gemm1_ms / 1e3
+    if cfg == 1:
+        achieved = nbytes["gemm1"] / g1_s / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+        roof["kernel"] = "stream_gemm_kernel (expert GEMM 1: w1/w3 + SwiGLU, weight streaming)"
+    else:
+        # the MFMA instructions the kernel issues are bf16 (fp8 weights are
+        # widened to bf16 in registers) or fp32: that dtype's peak
+        peak = FP32_PEAK_TFLOPS if wl.act_dtype == "f32" else BF16_PEAK_TFLOPS
+        achieved = flops["gemm1"] / g1_s / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak}
+        roof["kernel"] = ("grouped_gemm_kernel (fp32 MFMA" if wl.act_dtype == "f32"
+                          else "dma_gemm_kernel (bf16 MFMA") + ", expert GEMM 1 + activation)"
+        if wl.w_dtype == "fp8":
+            roof["frac_of_fp8_peak"] = achieved / FP8_PEAK_TFLOPS
+    roof["traffic"] = traffic_from_profiles(cfg, w_layout)
+    roof["algorithmic_bytes"] = nbytes["gemm1"]
+    roof["algorithmic_flops"] = flops["gemm1"]
+    return roof
+
+
+def other_workload(M, cfg: int, hip, w_layout_arg, K: int = 20, W: int = 3):
+    """Tokens/s and the first expert GEMM's roofline of another workload,
+    timed as the main one on fewer steps (no stage breakdown, no extras)."""
+    import numpy as np
+    import torch
+    from synth import make_workload
+    print(f"[bench] other workload {cfg}", file=sys.stderr, flush=True)
+    wl = make_workload(cfg)
+    w_layout = w_layout_arg or ("rowmajor" if wl.act_dtype == "f32" else "tiled")
+    layer = M.MoELayer(wl, device="cuda:0", keep_logits=False,
+                       w_layout=M.MOE_W_TILED16 if w_layout == "tiled" else M.MOE_W_ROWMAJOR)
+    wall, gemm1_ms = timed_steps(layer, K, W, hip)
+    res = layer.results()
+    off = res["off"]
+    kept_rows = int(off[wl.e_end] - off[wl.e_begin])
+    used = int(np.count_nonzero(res["kept"][wl.e_begin:wl.e_end]))
+    shared = wl.shared is not None
+    nbytes = algorithmic_bytes(wl, kept_rows, used, shared, sent_rows=int(off[wl.E]))
+    flops = gemm_flops(wl, kept_rows, shared)
+    roof = dominant_roofline(wl, cfg, gemm1_ms, nbytes, flops, w_layout)
+    del layer
+    torch.cuda.empty_cache()
+    return {"workload": f"{wl.name}: T={wl.T}, d={wl.d}, E={wl.E}, top-{wl.k}, {wl.act} "
+                        f"h={wl.h}{' + shared' if shared else ''}, capacity "
+                        f"{'none' if wl.cf is None else wl.cf}",
+            "value": wl.T * K / wall, "unit": "tokens/s", "steps": K, "warmup": W,
+            "ms_per_step": wall * 1e3 / K, "gemm1_ms_timed": gemm1_ms,
+            "dtype": wl.act_dtype if wl.w_dtype != "fp8" else "bf16 (fp8 e4m3 weights)",
+            "expert_weight_layout": w_layout, "roofline": roof}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=2,
-                    help="workload index 0-4 (default 2: the prefill-shaped Mixtral layer)")
+    ap.add_argument("--config", type=int, default=None,
+                    help=f"workload index 0-4 (default {DEFAULT_CONFIG}: the prefill-shaped "
+                         "Mixtral layer, plus a short pass over the other four)")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="without --config: skip the pass over the other four workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--w-layout", choices=["rowmajor", "tiled"], default=None,
                     help="expert weight layout (default: tiled, re-laid out once at load time, "
@@ -290,6 +375,9 @@ def main():
                     help="instead of the layer: time a plain device copy of MIB MiB (HBM "
                          "calibration for the traffic counters) and a full read (sum)")
     args = ap.parse_args()
+    others = args.config is None and not args.no_other_workloads
+    if args.config is None:
+        args.config = DEFAULT_CONFIG
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU's share of the MoE layer; runs on more than one GPU "
               "are not part of this build (no collectives). Use --gpus 1.", file=sys.stderr)
@@ -318,22 +406,8 @@ def main():
     hip = _hip()
     K, W = args.steps, args.warmup
     print(f"[bench] warmup {W}, timed {K}", file=sys.stderr, flush=True)
-    for _ in range(W):
-        layer.forward()
-    torch.cuda.synchronize()
-    # Timed region: only the two events around the first expert GEMM are
-    # recorded (each recorded event delays the next kernel by a few
-    # microseconds); they give the dominant kernel's duration per step.
+    wall, gemm1_ms = timed_steps(layer, K, W, hip)
     n = M.MOE_LAYER_EVENTS
-    ev = Events(hip, 2 * K)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(K):
-        layer.forward(events=[None, None, ev.ev[2 * s], ev.ev[2 * s + 1], None, None])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gemm1_ms = float(np.mean([ev.ms(2 * s, 2 * s + 1) for s in range(K)]))
-    ev.close()
     ms_per_step = wall * 1e3 / K
     value = wl.T * K / wall
 
@@ -374,28 +448,7 @@ def main():
     shared = wl.shared is not None
     nbytes = algorithmic_bytes(wl, kept_rows, used, shared, sent_rows=int(off[wl.E]))
     flops = gemm_flops(wl, kept_rows, shared)
-    # the dominant kernel: the first expert GEMM (streams w1 and w3)
-    g1_s = gemm1_ms / 1e3  # measured in the timed region
-    bound = "hbm" if args.config == 1 else "mfma"
-    if bound == "hbm":
-        achieved = nbytes["gemm1"] / g1_s / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS}
-        roof["kernel"] = "stream_gemm_kernel (expert GEMM 1: w1/w3 + SwiGLU, weight streaming)"
-    else:
-        # the MFMA instructions the kernel issues are bf16 (fp8 weights are
-        # widened to bf16 in registers) or fp32: that dtype's peak
-        peak = FP32_PEAK_TFLOPS if wl.act_dtype == "f32" else BF16_PEAK_TFLOPS
-        achieved = flops["gemm1"] / g1_s / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": achieved / peak}
-        roof["kernel"] = ("grouped_gemm_kernel (fp32 MFMA" if wl.act_dtype == "f32"
-                          else "dma_gemm_kernel (bf16 MFMA") + ", expert GEMM 1 + activation)"
-        if wl.w_dtype == "fp8":
-            roof["frac_of_fp8_peak"] = achieved / FP8_PEAK_TFLOPS
-    roof["traffic"] = traffic_from_profiles(args.config, w_layout)
-    roof["algorithmic_bytes"] = nbytes["gemm1"]
-    roof["algorithmic_flops"] = flops["gemm1"]
+    roof = dominant_roofline(wl, args.config, gemm1_ms, nbytes, flops, w_layout)
     stage_frac = {st: (nbytes[st] / (stage_ms[st] / 1e3) / 1e9) / HBM_PEAK_GBS for st in STAGES}
 
     out = {
@@ -430,6 +483,11 @@ def main():
         "roofline": roof,
     }
     out["extras"] = extras(M, wl, layer, hip, args)
+    if others:
+        del layer
+        torch.cuda.empty_cache()
+        out["other_workloads"] = {
+            str(c): other_workload(M, c, hip, args.w_layout) for c in range(5) if c != args.config}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl)

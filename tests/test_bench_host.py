@@ -61,5 +61,4 @@ def test_cpu_sample_keeps_weights_and_cuts_tokens():
 
 def test_default_workload_is_the_prefill_layer():
     B = _bench()
-    src = open(os.path.join(ROOT, "bench.py")).read()
-    assert '"--config", type=int, default=2' in src
+    assert B.DEFAULT_CONFIG == 2
