@@ -95,3 +95,35 @@ def test_noalloc_refuses_layers_beyond_the_scratch():
     assert ei.value.status == MOE_ERR_WORKSPACE
     torch.cuda.synchronize()
     assert (to_host(layer.y) == to_host(torch.full_like(layer.y, 3.0))).all()  # nothing launched
+
+
+@pytest.mark.parametrize("cfg,over", [(1, dict(T=64, d=512, h=768)),
+                                      (2, dict(T=1000, d=512, h=640)),
+                                      (4, dict(T=256, d=512, h=256))])
+def test_noalloc_in_hip_graph(cfg, over):
+    """Code under HIP graph capture is among the callers the no-allocation
+    entry point is for: after one eager call (which looks up the scratch's
+    device address), the captured forward replays bit for bit equal to the
+    workspace entry point's outputs, with eager work between the replays."""
+    from expert_token_routing_gemm_amd import MoELayer
+    wl = make_workload(cfg, **over)
+    _say(f"[noalloc graph] cfg{cfg} T={wl.T} d={wl.d} h={wl.h}")
+    layer = MoELayer(wl)
+    layer.forward()
+    ref = _snapshot(layer)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer.forward_noalloc()  # eager call on the capture-side stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer.forward_noalloc()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        _clear(layer)  # eager work on the outputs between replays
+        graph.replay()
+        got = _snapshot(layer)
+        for k, v in ref.items():
+            np.testing.assert_array_equal(got[k], v, err_msg=k)
