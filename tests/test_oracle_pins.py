@@ -405,6 +405,40 @@ def test_combine_closed_form_identity_experts():
     np.testing.assert_array_equal(res["y"][gone], x64[gone])
 
 
+def test_executed_experts_use_their_own_weights_closed_form():
+    """A rank executes experts [e_begin, e_end) and holds only their weights,
+    local index e - e_begin.  With W1 = I and W2 = (e + 1) I for expert e
+    (its global index baked into the weights), positive x and relu:
+    y = x (1 + sum over kept assignments to executed experts of w (e + 1)),
+    the sampled-check helpers give (e + 1) x for expert e's rows and 7 x for
+    a shared expert with W2 = 7 I.  Catches: weights looked up by global
+    instead of local index, work done for experts of other ranks, a shared
+    expert left out or counted twice."""
+    d = 8
+    w = _workload_like(T=40, d=d, E=6, k=2, h=d, act="relu", R=3, seed=6, cf=None, shared=True)
+    w.e_begin, w.e_end = 2, 4
+    w.x = np.abs(w.x) + np.float32(0.25)
+    n = w.e_end - w.e_begin
+    w.w1 = np.stack([np.eye(d, dtype=np.float32)] * n)
+    w.w2 = np.stack([np.float32(e + 1) * np.eye(d, dtype=np.float32)
+                     for e in range(w.e_begin, w.e_end)])
+    w.shared = dict(w1=np.eye(d, dtype=np.float32), w3=None,
+                    w2=np.float32(7.0) * np.eye(d, dtype=np.float32))
+    res = O.layer(w)
+    ids, wts = res["route"]["ids"], res["route"]["weights"]
+    slot = res["dispatch"]["slot"]
+    mine = (slot >= 0) & (ids >= w.e_begin) & (ids < w.e_end)
+    gain = np.where(mine, wts * (ids + 1), 0.0).sum(1)
+    x64 = w.x.astype(np.float64)
+    assert mine.any() and (~mine).any()
+    np.testing.assert_allclose(res["y"], x64 * (1 + 7 + gain)[:, None], rtol=1e-13)
+    for e in range(w.e_begin, w.e_end):
+        np.testing.assert_allclose(O.expert_rows(w, x64[:5], e), (e + 1) * x64[:5], rtol=1e-14)
+    np.testing.assert_allclose(O.shared_rows(w, x64[:5]), 7 * x64[:5], rtol=1e-14)
+    np.testing.assert_allclose(O.token_outputs(w, np.arange(40), ids, wts, slot), res["y"],
+                               rtol=1e-13)
+
+
 # ---------------------------------------------------------------- P9 formats
 
 
